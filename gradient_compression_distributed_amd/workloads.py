@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the gradient-compression hot path.
+
+This module only draws random numbers.  It holds none of the method's
+arithmetic (no thresholds, codes, packing or norms), so the oracle and the
+HIP path can both be fed from it without sharing any of the computation.
+
+Every host stream is numpy PCG64 keyed by
+``SeedSequence([BASE_SEED, config_id, step, block])``.  The workloads are
+stand-ins for the pages' settings:
+
+1. gc2, W=1: N=65,541 (a ragged tail of 5 elements), g ~ N(0, 0.5^2) fresh
+   per step, r = 0, t = 0.5 (the threshold in the MXNet PR's usage examples),
+   3 steps.
+2. gc2 on a ResNet-50-sized flat gradient (25,557,032 elements, ResNet50's
+   25M parameters in the QSGD experiments table): 1,048,576-element blocks,
+   each N(0, sigma_b^2), sigma_b log-uniform in [1e-4, 1e-1] (fixed per block
+   across steps), values fresh per step; t = 0.01; 10 steps.
+3. Dequantize-and-reduce: W = 16 packed buffers of 25,557,032 elements whose
+   2-bit fields are i.i.d. with P(11) = P(10) = 0.05, P(00) = 0.9; t = 0.01.
+4. QSGD: 61,100,840 elements (AlexNet's 62M parameters in the same table)
+   ~ N(0, 0.01^2); d = 512, s = 7; one hash seed per step.
+5. Fused buckets: 2^30 elements in 128 buckets of 8,388,608, sigma_b
+   log-uniform in [1e-5, 1e-2] per bucket, t = 1e-3, 5 steps.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BASE_SEED = 20261202
+SIGMA_STREAM = 0xFFFFFFF  # the "step" slot of the per-block sigma stream
+
+
+def rng(config_id: int, step: int, block: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([BASE_SEED, config_id, step, block])))
+
+
+@dataclass(frozen=True)
+class Config:
+    cid: int
+    name: str
+    n: int
+    t: float = 0.0
+    steps: int = 1
+    block: int = 0           # block / bucket length (0: one block)
+    sigma: float = 0.0       # fixed sigma (configs 1 and 4)
+    sigma_lo: float = 0.0    # log-uniform sigma range per block
+    sigma_hi: float = 0.0
+    workers: int = 1
+    d: int = 0
+    s: int = 0
+
+
+CONFIGS = {
+    1: Config(1, "gc2 quantize+residual, W=1, ragged tail", 65_541, t=0.5, steps=3, sigma=0.5),
+    2: Config(2, "gc2 quantize+residual, ResNet-50-sized flat gradient", 25_557_032, t=0.01,
+              steps=10, block=1_048_576, sigma_lo=1e-4, sigma_hi=1e-1),
+    3: Config(3, "dequantize-and-reduce, 16 simulated workers", 25_557_032, t=0.01, workers=16),
+    4: Config(4, "QSGD stochastic quantize+dequantize", 61_100_840, sigma=0.01, d=512, s=7),
+    5: Config(5, "fused-bucket gc2 quantize+residual, 1G elements", 1 << 30, t=1e-3, steps=5,
+              block=8_388_608, sigma_lo=1e-5, sigma_hi=1e-2),
+}
+
+
+def block_sigmas(cfg: Config) -> np.ndarray:
+    """Per-block standard deviations, log-uniform in [sigma_lo, sigma_hi]."""
+    nblocks = (cfg.n + cfg.block - 1) // cfg.block
+    u = rng(cfg.cid, SIGMA_STREAM, 0).uniform(np.log10(cfg.sigma_lo), np.log10(cfg.sigma_hi),
+                                              nblocks)
+    return (10.0 ** u).astype(np.float64)
+
+
+def normal_block(cfg_id: int, step: int, block: int, n: int, sigma: float) -> np.ndarray:
+    g = rng(cfg_id, step, block).standard_normal(n, dtype=np.float32)
+    g *= np.float32(sigma)
+    return g
+
+
+def gradient(cfg: Config, step: int) -> np.ndarray:
+    """The whole float32 gradient of a config at a step (host memory)."""
+    if cfg.block == 0:
+        return normal_block(cfg.cid, step, 0, cfg.n, cfg.sigma)
+    out = np.empty(cfg.n, dtype=np.float32)
+    sig = block_sigmas(cfg)
+    for b in range(len(sig)):
+        lo = b * cfg.block
+        hi = min(lo + cfg.block, cfg.n)
+        out[lo:hi] = normal_block(cfg.cid, step, b, hi - lo, sig[b])
+    return out
+
+
+def gradient_block(cfg: Config, step: int, b: int) -> np.ndarray:
+    """One block (bucket) of a blocked config's gradient."""
+    sig = block_sigmas(cfg)
+    lo = b * cfg.block
+    hi = min(lo + cfg.block, cfg.n)
+    return normal_block(cfg.cid, step, b, hi - lo, sig[b])
+
+
+def iid_field_words(gen: np.random.Generator, nwords: int, p11: float = 0.05,
+                    p10: float = 0.05) -> np.ndarray:
+    """Random 32-bit words whose sixteen 2-bit fields are i.i.d.:
+    0b11 with probability p11, 0b10 with p10, else 0b00.
+
+    Fields are independent and identically distributed, so which field goes
+    to which bit pair does not matter; field k is put at bits 2k..2k+1."""
+    out = np.zeros(nwords, dtype=np.uint32)
+    chunk = 1 << 20
+    for lo in range(0, nwords, chunk):
+        hi = min(lo + chunk, nwords)
+        u = gen.random((hi - lo, 16), dtype=np.float32)
+        f = np.where(u < p11, 3, np.where(u < p11 + p10, 2, 0)).astype(np.uint32)
+        f <<= (2 * np.arange(16, dtype=np.uint32))[None, :]
+        out[lo:hi] = np.bitwise_or.reduce(f, axis=1)
+    return out
+
+
+def worker_words(cfg: Config, worker: int, nwords: int) -> np.ndarray:
+    return iid_field_words(rng(cfg.cid, 0, worker), nwords)
+
+
+def qsgd_seed(step: int) -> int:
+    """64-bit hash seed of a QSGD step."""
+    return (BASE_SEED << 24) | (step & 0xFFFFFF)
+
+
+def qsgd_spiky(n: int, d: int, seed: int) -> np.ndarray:
+    """Buckets holding 1..8 large entries of random sign over small noise, so
+    that every level 0..s occurs (a plain Gaussian bucket almost never goes
+    past level 2)."""
+    gen = np.random.Generator(np.random.PCG64(np.random.SeedSequence([BASE_SEED, 44, seed])))
+    g = gen.standard_normal(n, dtype=np.float32) * np.float32(1e-4)
+    nb = (n + d - 1) // d
+    for b in range(nb):
+        lo, hi = b * d, min(b * d + d, n)
+        k = int(gen.integers(1, 9))
+        k = min(k, hi - lo)
+        pos = lo + gen.choice(hi - lo, size=k, replace=False)
+        mag = gen.uniform(0.05, 1.0, size=k).astype(np.float32)
+        sgn = np.where(gen.random(k) < 0.5, -1.0, 1.0).astype(np.float32)
+        g[pos] = mag * sgn
+    return g
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation (torch) for the 1G-element benchmark workload, where
+# drawing 4 GiB per step on the host would dominate the run.  Same shapes and
+# distributions, a torch (Philox) stream seeded from the same base seed.
+# ---------------------------------------------------------------------------
+
+def device_generator(cfg_id: int, step: int, device="cuda"):
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed((BASE_SEED * 1000 + cfg_id * 100 + step) & 0x7FFFFFFFFFFFFFFF)
+    return gen
+
+
+def fill_bucketed_normal_(out, cfg: Config, step: int):
+    """Fill a device float32 tensor of cfg.n elements with the config's
+    per-bucket N(0, sigma_b^2) gradient."""
+    import torch
+
+    gen = device_generator(cfg.cid, step, out.device)
+    sig = torch.tensor(block_sigmas(cfg), dtype=torch.float32, device=out.device)
+    nb = len(sig)
+    for b in range(nb):
+        lo = b * cfg.block
+        hi = min(lo + cfg.block, cfg.n)
+        seg = out[lo:hi]
+        seg.normal_(0.0, 1.0, generator=gen)
+        seg.mul_(sig[b])
+    return out
+
+
+def fill_iid_field_words_(out, cfg_id: int, worker: int, p11: float = 0.05, p10: float = 0.05):
+    """Device twin of iid_field_words: fill an int32 tensor with words whose
+    16 two-bit fields are i.i.d. (field k at bits 2k..2k+1)."""
+    import torch
+
+    gen = device_generator(cfg_id, 1000 + worker, out.device)
+    chunk = 1 << 22
+    shifts = (2 * torch.arange(16, device=out.device, dtype=torch.int64))
+    for lo in range(0, out.numel(), chunk):
+        hi = min(lo + chunk, out.numel())
+        u = torch.rand((hi - lo, 16), generator=gen, device=out.device)
+        f = torch.where(u < p11, 3, torch.where(u < p11 + p10, 2, 0)).to(torch.int64)
+        w = (f << shifts).sum(dim=1)
+        out[lo:hi] = (w - ((w >> 31) << 32)).to(torch.int32)
+    return out

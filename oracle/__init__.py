@@ -1,0 +1,185 @@
+"""CPU oracle for the gradient-compression hot path (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never loads it and must fail loudly when the HIP
+extension is missing instead of falling back here.
+
+The arithmetic lives in ``gcq_oracle.c`` (plain scalar C, one thread); this
+module only marshals numpy arrays through ctypes.  Each wrapper names the
+passage of the pages it follows:
+
+* ``gc2_quantize``       -- MXNet PR "2bit gradient compression",
+  "Two bit quantization" and "Format of compressed gradient"; CD-SGD 3.4.1.
+* ``gc2_dequant_reduce`` -- same PR, "Local kvstore" (device 0 dequantizes
+  and sums the other devices' packed data), fixed worker order.
+* ``qsgd_norms`` / ``qsgd_levels`` / ``qsgd_quantize`` / ``qsgd_dequant``
+  -- QSGD summary, Knowl 1 (Q_s), Knowl 2 (norm/sign/level tuple),
+  Knowl 8 (bucketing).
+* ``philox4x32_10`` / ``uniform`` -- the SC'11 Philox-4x32 generator.  The
+  pages name no random source, so the exact uniform stream is
+  "parity unpinned" by the pages; it is pinned only statistically.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from .build import build_oracle
+
+        build_oracle()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, u32, u64, f32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32,
+                             ctypes.c_uint64, ctypes.c_float)
+    lib.oracle_gc2_quantize.argtypes = [vp, vp, sz, f32, vp]
+    lib.oracle_gc2_quantize.restype = None
+    lib.oracle_gc2_dequant_reduce.argtypes = [vp, u32, sz, f32, vp]
+    lib.oracle_gc2_dequant_reduce.restype = None
+    lib.oracle_philox4x32_10.argtypes = [vp, vp, vp]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_uniform.argtypes = [u64, u64]
+    lib.oracle_uniform.restype = f32
+    lib.oracle_qsgd_norms.argtypes = [vp, sz, u32, vp]
+    lib.oracle_qsgd_norms.restype = None
+    lib.oracle_qsgd_levels.argtypes = [vp, sz, u32, u32, u64, u64, vp, vp]
+    lib.oracle_qsgd_levels.restype = None
+    lib.oracle_qsgd_quantize.argtypes = [vp, sz, u32, u32, u64, vp, vp]
+    lib.oracle_qsgd_quantize.restype = None
+    lib.oracle_qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp]
+    lib.oracle_qsgd_dequant.restype = None
+    _lib = lib
+    return lib
+
+
+def _f32(a, name):
+    if not (isinstance(a, np.ndarray) and a.dtype == np.float32 and a.flags.c_contiguous):
+        raise TypeError(f"{name} must be a C-contiguous float32 numpy array")
+    return a
+
+
+def _u32(a, name):
+    if not (isinstance(a, np.ndarray) and a.dtype == np.uint32 and a.flags.c_contiguous):
+        raise TypeError(f"{name} must be a C-contiguous uint32 numpy array")
+    return a
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def packed_words(n: int) -> int:
+    return (n + 15) // 16
+
+
+def nibble_words(n: int) -> int:
+    return (n + 7) // 8
+
+
+def num_buckets(n: int, d: int) -> int:
+    return (n + d - 1) // d
+
+
+def gc2_quantize(g: np.ndarray, r: np.ndarray, t: float, out: np.ndarray | None = None):
+    """One quantize step: returns packed words; ``r`` is updated in place."""
+    lib = _load()
+    _f32(g, "g"), _f32(r, "r")
+    n = g.size
+    if r.size != n:
+        raise ValueError("g and r differ in size")
+    if out is None:
+        out = np.empty(packed_words(n), dtype=np.uint32)
+    _u32(out, "out")
+    if out.size < packed_words(n):
+        raise ValueError("out too small")
+    lib.oracle_gc2_quantize(_ptr(g), _ptr(r), n, ctypes.c_float(t), _ptr(out))
+    return out
+
+
+def gc2_dequant_reduce(words: list, n: int, t: float, acc: np.ndarray | None = None):
+    """Sum of W workers' dequantized codes, worker order 0..W-1, float32."""
+    lib = _load()
+    W = len(words)
+    for w in words:
+        _u32(w, "words[w]")
+        if w.size < packed_words(n):
+            raise ValueError("a worker buffer is too small")
+    if acc is None:
+        acc = np.empty(n, dtype=np.float32)
+    _f32(acc, "acc")
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[w.ctypes.data for w in words])
+    lib.oracle_gc2_dequant_reduce(ctypes.cast(ptrs, ctypes.c_void_p), W, n,
+                                  ctypes.c_float(t), _ptr(acc))
+    return acc
+
+
+def philox4x32_10(ctr, key):
+    lib = _load()
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    o = np.empty(4, dtype=np.uint32)
+    lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(o))
+    return o
+
+
+def uniform(seed: int, i: int) -> float:
+    return float(_load().oracle_uniform(seed, i))
+
+
+def qsgd_norms(g: np.ndarray, d: int) -> np.ndarray:
+    lib = _load()
+    _f32(g, "g")
+    norms = np.empty(num_buckets(g.size, d), dtype=np.float32)
+    lib.oracle_qsgd_norms(_ptr(g), g.size, d, _ptr(norms))
+    return norms
+
+
+def qsgd_levels(g: np.ndarray, d: int, s: int, seed: int, norms: np.ndarray,
+                index_base: int = 0) -> np.ndarray:
+    """Nibbles for the slice ``g`` given bucket norms (e.g. a GPU's norms).
+
+    ``index_base`` is the global index of ``g[0]``; it must be a multiple of
+    ``d`` and of 8 (buckets and words are counted from the slice start, the
+    uniform uses the global index)."""
+    lib = _load()
+    _f32(g, "g"), _f32(norms, "norms")
+    if index_base % d or index_base % 8:
+        raise ValueError("index_base must be a multiple of d and 8")
+    if norms.size < num_buckets(g.size, d):
+        raise ValueError("norms too small")
+    nib = np.empty(nibble_words(g.size), dtype=np.uint32)
+    lib.oracle_qsgd_levels(_ptr(g), g.size, d, s, ctypes.c_uint64(seed),
+                           ctypes.c_uint64(index_base), _ptr(norms), _ptr(nib))
+    return nib
+
+
+def qsgd_quantize(g: np.ndarray, d: int, s: int, seed: int):
+    lib = _load()
+    _f32(g, "g")
+    norms = np.empty(num_buckets(g.size, d), dtype=np.float32)
+    nib = np.empty(nibble_words(g.size), dtype=np.uint32)
+    lib.oracle_qsgd_quantize(_ptr(g), g.size, d, s, ctypes.c_uint64(seed),
+                             _ptr(norms), _ptr(nib))
+    return norms, nib
+
+
+def qsgd_dequant(norms: np.ndarray, nibbles: np.ndarray, n: int, d: int, s: int) -> np.ndarray:
+    lib = _load()
+    _f32(norms, "norms"), _u32(nibbles, "nibbles")
+    if nibbles.size < nibble_words(n) or norms.size < num_buckets(n, d):
+        raise ValueError("inputs too small")
+    out = np.empty(n, dtype=np.float32)
+    lib.oracle_qsgd_dequant(_ptr(norms), _ptr(nibbles), n, d, s, _ptr(out))
+    return out

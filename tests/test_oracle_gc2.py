@@ -1,0 +1,224 @@
+"""Pins of the CPU oracle's 2-bit quantizer against what the pages fix.
+
+MXNet PR "2bit gradient compression": "Two bit quantization" (codes, >= tie
+rule, residual carried into the next step), "Format of compressed gradient"
+(16 codes per 32-bit element, first code leftmost, the worked example);
+CD-SGD 3.4.1 (a code that passes is worth the threshold itself)."""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from gradient_compression_distributed_amd import workloads as wl
+from tests import brute
+
+F = np.float32
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxnet_pr8662_example.txt")
+
+
+def _golden():
+    d = {}
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, rest = line.partition(" ")
+        d[key] = rest
+    return d
+
+
+def test_pr_worked_example():
+    gd = _golden()
+    t = float(gd["threshold"])
+    g = np.array([F(x) for x in gd["input"].split()], dtype=np.float32)
+    r = np.zeros_like(g)
+    words = oracle.gc2_quantize(g, r, t)
+    assert words.size == 1
+    assert int(words[0]) == int(gd["word"], 16)
+    assert format(int(words[0]), "032b") == gd["bits"].replace(" ", "")
+    expect_r = np.array([F(x) for x in gd["residual"].split()], dtype=np.float32)
+    assert np.array_equal(r.view(np.uint32), expect_r.view(np.uint32))
+
+
+@pytest.mark.parametrize("n", [65_541, 25_557_032, 1 << 30, 16, 17, 1])
+def test_size_is_one_sixteenth(n):
+    # ceil(n/16) words: 4,097 / 1,597,315 / 67,108,864 at the three gc2 sizes
+    expect = {65_541: 4_097, 25_557_032: 1_597_315, 1 << 30: 67_108_864}
+    words = oracle.packed_words(n)
+    if n in expect:
+        assert words == expect[n]
+    assert words * 16 >= n > (words - 1) * 16
+    if n % 16 == 0:
+        assert Fraction(words * 4, n * 4) == Fraction(1, 16)
+
+
+@pytest.mark.parametrize("n", [1, 5, 15, 16, 17, 33])
+def test_writes_exactly_ceil_n_over_16_words(n):
+    g = np.random.default_rng(n).standard_normal(n).astype(np.float32)
+    r = np.zeros(n, np.float32)
+    nw = oracle.packed_words(n)
+    out = np.full(nw + 3, 0xDEADBEEF, dtype=np.uint32)
+    oracle.gc2_quantize(g, r, 0.5, out)
+    assert np.all(out[nw:] == 0xDEADBEEF)
+    tail = n % 16
+    if tail:
+        assert int(out[nw - 1]) & ((1 << (32 - 2 * tail)) - 1) == 0
+
+
+def _adversarial(t):
+    t = F(t)
+    inf = F(np.inf)
+    return [t, -t, np.nextafter(t, F(0)), np.nextafter(-t, F(0)), np.nextafter(t, inf),
+            np.nextafter(-t, -inf), F(0.0), F(-0.0), F(2) * t, -F(2) * t, F(1e-30), F(-1e-30),
+            F(1e30), F(-1e30), F(np.nan), inf, -inf, F(1.5e-45)]
+
+
+@pytest.mark.parametrize("t", [0.5, 0.01, 2.0, 1e-3])
+def test_brute_force_every_small_n(t):
+    rs = np.random.default_rng(int(t * 1e6))
+    adv = _adversarial(t)
+    for n in range(1, 64):
+        g = rs.normal(0, 2 * t, n).astype(np.float32)
+        r = rs.normal(0, 0.5 * t, n).astype(np.float32)
+        # sprinkle adversarial values into g and r
+        k = rs.integers(0, n + 1)
+        pos = rs.choice(n, size=k, replace=False)
+        for p in pos:
+            if rs.random() < 0.5:
+                g[p], r[p] = adv[rs.integers(len(adv))], F(0.0)
+            else:
+                g[p] = adv[rs.integers(len(adv))]
+        want_words, want_r = brute.gc2_bits(g, r, t)
+        rr = r.copy()
+        words = oracle.gc2_quantize(g, rr, t)
+        assert [int(w) for w in words] == want_words, n
+        assert np.array_equal(rr.view(np.uint32), np.array(want_r, np.float32).view(np.uint32)), n
+
+
+def test_exhaustive_code_patterns():
+    t = F(0.25)
+    pick = {0: F(0.0), 1: t, 2: -t}           # pattern digit -> value giving 00 / 11 / 10
+    text_of = {0: "00", 1: "11", 2: "10"}
+    pats = np.array(np.meshgrid(*[np.arange(3)] * 8, indexing="ij")).reshape(8, -1).T
+    g = np.vectorize(pick.get, otypes=[np.float32])(pats).astype(np.float32).ravel()
+    r = np.zeros_like(g)
+    words = oracle.gc2_quantize(g, r, float(t))   # 6561 * 8 values, 2 patterns per word
+    for i, p in enumerate(pats):
+        w = int(words[i // 2])
+        half = format(w, "032b")[16 * (i % 2):16 * (i % 2) + 16]
+        assert half == "".join(text_of[x] for x in p)
+    assert np.all(r == 0)
+
+
+def _codes(words, n):
+    w = np.asarray(words, dtype=np.uint32)
+    k = np.arange(n)
+    return (w[k // 16] >> (30 - 2 * (k % 16)).astype(np.uint32)) & 3
+
+
+def _check_step_invariants(g, r_old, r_new, words, t):
+    n = g.size
+    c = _codes(words, n)
+    v = (g + r_old).astype(np.float32)
+    assert not np.any(c == 1), "code 01 is never produced"
+    assert np.all(r_new[c == 3] >= 0)
+    assert np.all(r_new[c == 2] <= 0)
+    z = c == 0
+    assert np.array_equal(r_new[z].view(np.uint32), v[z].view(np.uint32))
+    assert np.all(np.abs(r_new[z]) < F(t))
+    assert np.all(v[c == 3] >= F(t)) and np.all(v[c == 2] <= -F(t))
+    # error feedback: g + r_old == dq + r_new up to the two roundings.  Taken
+    # in float64, whose own rounding (if any) is far below the float32 bound;
+    # the exact-rational version is test_exact_identity_with_fractions.
+    dq = np.where(c == 3, np.float64(F(t)), np.where(c == 2, -np.float64(F(t)), 0.0))
+    lhs = g.astype(np.float64) + r_old.astype(np.float64)
+    rhs = dq + r_new.astype(np.float64)
+    bound = 0.5 * np.spacing(np.abs(v)).astype(np.float64) + \
+        0.5 * np.spacing(np.abs(r_new)).astype(np.float64)
+    assert np.all(np.abs(lhs - rhs) <= bound)
+    tail = n % 16
+    if tail:
+        assert int(words[-1]) & ((1 << (32 - 2 * tail)) - 1) == 0
+
+
+def test_invariants_config1_three_steps():
+    cfg = wl.CONFIGS[1]
+    r = np.zeros(cfg.n, np.float32)
+    for step in range(cfg.steps):
+        g = wl.gradient(cfg, step)
+        r_old = r.copy()
+        words = oracle.gc2_quantize(g, r, cfg.t)
+        assert words.size == 4_097
+        _check_step_invariants(g, r_old, r, words, cfg.t)
+
+
+def test_invariants_config2_blocks():
+    cfg = wl.CONFIGS[2]
+    sig = wl.block_sigmas(cfg)
+    assert len(sig) == 25 and np.all((sig >= 1e-4) & (sig <= 1e-1))
+    for b in (0, int(np.argmin(sig)), int(np.argmax(sig)), 24):
+        r = np.zeros(min(cfg.block, cfg.n - b * cfg.block), np.float32)
+        for step in range(3):
+            g = wl.gradient_block(cfg, step, b)
+            r_old = r.copy()
+            words = oracle.gc2_quantize(g, r, cfg.t)
+            _check_step_invariants(g, r_old, r, words, cfg.t)
+
+
+def test_exact_identity_with_fractions():
+    # The identity in exact rationals on adversarial magnitudes
+    t = 0.01
+    rs = np.random.default_rng(5)
+    g = (rs.standard_normal(400) * 10.0 ** rs.uniform(-8, 2, 400)).astype(np.float32)
+    r = (rs.standard_normal(400) * 10.0 ** rs.uniform(-8, 0, 400)).astype(np.float32)
+    r_old = r.copy()
+    words = oracle.gc2_quantize(g, r, t)
+    c = _codes(words, g.size)
+    for i in range(g.size):
+        v = F(g[i]) + F(r_old[i])
+        dq = {3: Fraction(float(F(t))), 2: -Fraction(float(F(t)))}.get(int(c[i]), Fraction(0))
+        err = abs(Fraction(float(g[i])) + Fraction(float(r_old[i])) - dq - Fraction(float(r[i])))
+        bound = Fraction(float(np.spacing(abs(v)))) / 2 + Fraction(float(np.spacing(abs(r[i])))) / 2
+        assert err <= bound
+
+
+def test_ieee_special_values():
+    # NaN/Inf/-0 follow plain IEEE float32: nothing is special-cased
+    t = 0.5
+    g = np.array([np.nan, np.inf, -np.inf, -0.0, 0.5, -0.5, np.nextafter(F(0.5), F(0)), -0.0],
+                 dtype=np.float32)
+    r = np.zeros_like(g)
+    r[3] = -0.0                                    # -0 + -0 = -0; -0 + +0 = +0
+    words = oracle.gc2_quantize(g, r, t)
+    c = _codes(words, g.size)
+    assert list(c) == [0, 3, 2, 0, 3, 2, 0, 0]
+    assert np.isnan(r[0])
+    assert r[1] == np.inf and r[2] == -np.inf
+    assert r[3] == 0 and np.signbit(r[3])
+    assert r[7] == 0 and not np.signbit(r[7])
+    assert r[4] == 0 and r[5] == 0
+    assert r[6] == np.nextafter(F(0.5), F(0))
+
+
+def test_residual_carries_over_and_resumes():
+    # the residual is the only state; resuming from a copy is identical
+    cfg = wl.CONFIGS[1]
+    r = np.zeros(cfg.n, np.float32)
+    outs = []
+    for step in range(3):
+        outs.append(oracle.gc2_quantize(wl.gradient(cfg, step), r, cfg.t))
+    r2 = np.zeros(cfg.n, np.float32)
+    oracle.gc2_quantize(wl.gradient(cfg, 0), r2, cfg.t)
+    saved = r2.copy()
+    fresh = saved.copy()
+    w1 = oracle.gc2_quantize(wl.gradient(cfg, 1), fresh, cfg.t)
+    w2 = oracle.gc2_quantize(wl.gradient(cfg, 2), fresh, cfg.t)
+    assert np.array_equal(w1, outs[1]) and np.array_equal(w2, outs[2])
+    assert np.array_equal(fresh.view(np.uint32), r.view(np.uint32))
+    # a small value below threshold is eventually sent once accumulated
+    g = np.full(1, 0.2, np.float32)
+    rr = np.zeros(1, np.float32)
+    codes = [int(_codes(oracle.gc2_quantize(g, rr, 0.5), 1)[0]) for _ in range(3)]
+    assert codes == [0, 0, 3]

@@ -1,0 +1,228 @@
+"""Pins of the oracle's QSGD quantizer against what the QSGD summary fixes.
+
+Knowl 1: Q_s(v_i) = ||v||_2 sgn(v_i) xi_i with xi_i in {l/s, (l+1)/s},
+P(upper) = a s - l; sgn(0) = +1; Q_s(0) = 0; E[Q] = v; variance bound
+min(n/s^2, sqrt(n)/s) ||v||^2; E||Q||_0 <= s(s + sqrt(n)).  Knowl 2: the
+(norm, sign, level) tuple.  Knowl 8: contiguous buckets of d, one scale per
+bucket, variance bound with d in place of n."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from gradient_compression_distributed_amd import workloads as wl
+from tests import brute
+
+F = np.float32
+
+
+def _nibbles(words, n):
+    w = np.asarray(words, dtype=np.uint32)
+    k = np.arange(n)
+    return (w[k // 8] >> (28 - 4 * (k % 8)).astype(np.uint32)) & 15
+
+
+def _q(g, d, s, seed):
+    norms, nib = oracle.qsgd_quantize(g, d, s, seed)
+    return norms, nib, oracle.qsgd_dequant(norms, nib, g.size, d, s)
+
+
+# --------------------------------------------------------------- norms
+def test_norms_match_exact_sum():
+    rs = np.random.default_rng(1)
+    g = (rs.standard_normal(5000) * 10.0 ** rs.uniform(-6, 3, 5000)).astype(np.float32)
+    d = 37
+    norms = oracle.qsgd_norms(g, d)
+    assert norms.size == math.ceil(5000 / d)
+    for b in range(norms.size):
+        seg = g[b * d:(b + 1) * d].astype(np.float64)
+        exact = math.sqrt(math.fsum(x * x for x in seg))  # squares of float32 are exact in double
+        assert abs(float(norms[b]) - exact) <= 0.5 * float(np.spacing(F(exact))) * 1.000001
+
+
+def test_norms_constant_bucket_closed_form():
+    g = np.full(64, 0.5, np.float32)
+    assert list(oracle.qsgd_norms(g, 4)) == [1.0] * 16        # sqrt(4 * 0.25)
+    g = np.full(48, -0.25, np.float32)
+    assert list(oracle.qsgd_norms(g, 16)) == [1.0] * 3         # sqrt(16 / 16)
+    assert list(oracle.qsgd_norms(np.full(9, 3.0, np.float32), 9)) == [9.0]
+
+
+# ------------------------------------------------------- special cases
+@pytest.mark.parametrize("s", [1, 3, 7])
+def test_zero_bucket_is_zero(s):
+    g = np.zeros(40, np.float32)
+    g[::3] = -0.0
+    norms, nib, out = _q(g, 8, s, 5)
+    assert np.all(norms == 0) and np.all(nib == 0)     # -0 has sign bit 0 (sgn(0) = +1)
+    assert np.all(out == 0) and not np.any(np.signbit(out))
+
+
+@pytest.mark.parametrize("s", [1, 2, 5, 7])
+def test_single_nonzero_gets_top_level(s):
+    rs = np.random.default_rng(s)
+    d = 16
+    g = np.zeros(d * 50, np.float32)
+    pos = np.arange(50) * d + rs.integers(0, d, 50)
+    g[pos] = (rs.standard_normal(50) * 10.0 ** rs.uniform(-20, 20, 50)).astype(np.float32)
+    norms, nib, out = _q(g, d, s, 99)
+    lv = _nibbles(nib, g.size)
+    assert np.array_equal(norms, np.abs(g[pos]))     # the norm of one element is |g|
+    assert np.all(lv[pos] & 7 == s)
+    assert np.all((lv[pos] >> 3) == (g[pos] < 0))
+    mask = np.ones(g.size, bool)
+    mask[pos] = False
+    assert np.all(lv[mask] == 0)
+    np.testing.assert_allclose(out[pos], g[pos], rtol=1e-6)
+
+
+def test_exact_midpoint_levels():
+    # d = 4, all 0.5: norm 1, a = 0.5, x = 0.5 s exact; with s = 4 every level
+    # is exactly 2 whatever the uniforms
+    g = np.full(4000, 0.5, np.float32)
+    g[1::2] *= -1
+    for seed in range(5):
+        _, nib, out = _q(g, 4, 4, seed)
+        lv = _nibbles(nib, g.size)
+        assert np.all(lv & 7 == 2)
+        assert np.all((lv >> 3) == (g < 0))
+        assert np.array_equal(out, g)
+
+
+def test_s1_is_ternary():
+    rs = np.random.default_rng(2)
+    g = rs.standard_normal(4096).astype(np.float32)
+    norms, nib, out = _q(g, 64, 1, 3)
+    lv = _nibbles(nib, g.size) & 7
+    assert set(np.unique(lv)) <= {0, 1}
+    nb = np.repeat(norms, 64)
+    assert np.all((out == 0) | (np.abs(out) == nb))
+
+
+def test_sign_bit_even_at_level_zero():
+    g = np.array([1.0, -1e-6, 1e-6, -0.0, 0.0, -2.0, 0.5, -0.5], np.float32)
+    _, nib, out = _q(g, 8, 7, 1)
+    sg = _nibbles(nib, 8) >> 3
+    assert list(sg) == [0, 1, 0, 0, 0, 1, 0, 1]
+
+
+def test_levels_and_dequant_vs_bruteforce_decode():
+    g = wl.qsgd_spiky(3000, 64, 1)
+    s, d, seed = 7, 64, 12345
+    norms, nib, out = _q(g, d, s, seed)
+    lv = np.array(brute.nibbles_from_words(nib, g.size))
+    assert set(np.unique(lv & 7)) == set(range(8)), "spiky input must reach every level"
+    for i in range(g.size):
+        norm = F(norms[i // d])
+        level = int(lv[i] & 7)
+        a = F(abs(g[i])) / norm
+        x = a * F(s)
+        fl = math.floor(float(x))
+        u = F((brute.philox4x32_10([i >> 2, 0, 0, 0], [seed & 0xFFFFFFFF, seed >> 32])[i & 3] >> 8)
+              * 2.0 ** -24)
+        if x >= F(s):
+            want = s
+        else:
+            want = fl + (1 if u < F(x) - F(fl) else 0)
+        assert level == want, i
+        assert (lv[i] >> 3) == (1 if g[i] < 0 else 0)
+        # dequant: (norm * level) / s with two float32 roundings -> within
+        # one ulp of the exact rational, sign applied
+        exact = Fraction(float(norm)) * level / s
+        got = Fraction(float(abs(out[i])))
+        assert abs(got - exact) <= Fraction(float(np.spacing(F(float(exact)))))
+        assert np.signbit(out[i]) == bool(lv[i] >> 3)
+
+
+def test_slice_with_index_base_matches_whole():
+    g = wl.qsgd_spiky(4096, 512, 2)
+    norms, nib = oracle.qsgd_quantize(g, 512, 7, 77)
+    part = oracle.qsgd_levels(g[1024:2048].copy(), 512, 7, 77, norms[2:4].copy(), index_base=1024)
+    assert np.array_equal(part, nib[128:256])
+
+
+# ------------------------------------------------------------ statistics
+def test_unbiased_monte_carlo():
+    # E[Q_s(v)] = v, checked per coordinate with M independent seeds
+    rs = np.random.default_rng(4)
+    v = rs.standard_normal(10).astype(np.float32)
+    d, s, M = 4, 3, 1 << 16
+    acc = np.zeros(10, np.float64)
+    for seed in range(M):
+        _, _, out = _q(v, d, s, seed * 2654435761)
+        acc += out
+    mean = acc / M
+    norms = oracle.qsgd_norms(v, d).astype(np.float64)
+    nb = np.repeat(norms, d)[:10]
+    x = np.abs(v) / nb * s
+    p = x - np.floor(x)
+    sd = nb / s * np.sqrt(p * (1 - p))
+    assert np.all(np.abs(mean - v) <= 5 * sd / math.sqrt(M) + 1e-7)
+
+
+def test_variance_and_sparsity_bounds():
+    g = wl.normal_block(4, 0, 0, 512 * 64, 0.01)
+    d, s = 512, 7
+    norms = oracle.qsgd_norms(g, d).astype(np.float64)
+    err = np.zeros(64)
+    nnz = np.zeros(64)
+    R = 64
+    for seed in range(R):
+        _, nib, out = _q(g, d, s, 1000 + seed)
+        diff = (out.astype(np.float64) - g).reshape(64, d)
+        err += (diff ** 2).sum(1)
+        nnz += (out.reshape(64, d) != 0).sum(1)
+    bound = min(d / s ** 2, math.sqrt(d) / s) * norms ** 2
+    assert np.all(err / R <= bound)
+    assert np.all(nnz / R <= s * (s + math.sqrt(d)))
+
+
+def test_uniforms_are_uniform():
+    seed = wl.qsgd_seed(0)
+    u = np.array([oracle.uniform(seed, i) for i in range(200_000)], np.float64)
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert np.all(u * 2 ** 24 == np.floor(u * 2 ** 24))
+    assert abs(u.mean() - 0.5) < 5 * math.sqrt(1 / 12 / u.size)
+    counts = np.bincount((u * 256).astype(int), minlength=256)
+    chi2 = ((counts - u.size / 256) ** 2 / (u.size / 256)).sum()
+    assert chi2 < 255 + 6 * math.sqrt(2 * 255)
+    for lag in (1, 2, 3, 4, 5):
+        c = np.corrcoef(u[:-lag], u[lag:])[0, 1]
+        assert abs(c) < 5 / math.sqrt(u.size)
+    v = np.array([oracle.uniform(seed + 1, i) for i in range(50_000)])
+    assert abs(np.corrcoef(u[:50_000], v)[0, 1]) < 5 / math.sqrt(50_000)
+
+
+def test_philox_python_twin():
+    rs = np.random.default_rng(8)
+    for _ in range(200):
+        ctr = [int(x) for x in rs.integers(0, 1 << 32, 4, dtype=np.uint64)]
+        key = [int(x) for x in rs.integers(0, 1 << 32, 2, dtype=np.uint64)]
+        assert [int(x) for x in oracle.philox4x32_10(ctr, key)] == brute.philox4x32_10(ctr, key)
+
+
+def test_uniform_depends_on_global_index_only():
+    seed = (1 << 40) + 12345
+    for i in (0, 1, 2, 3, 4, 1 << 33, (1 << 34) + 7):
+        q = i >> 2
+        o = brute.philox4x32_10([q & 0xFFFFFFFF, q >> 32, 0, 0], [seed & 0xFFFFFFFF, seed >> 32])
+        assert oracle.uniform(seed, i) == (o[i & 3] >> 8) * 2.0 ** -24
+
+
+# A (seed, index) whose uniform is exactly 0 (found by a search over the
+# hash; the test re-checks it).  At an integral x = a*s the upper level has
+# probability p = 0 (Knowl 1), so even u = 0 must keep level l.
+U_ZERO_SEED, U_ZERO_INDEX = 20261202, 13_675_585
+
+
+def test_probability_zero_step_never_taken():
+    q = U_ZERO_INDEX >> 2
+    o = brute.philox4x32_10([q, 0, 0, 0], [U_ZERO_SEED & 0xFFFFFFFF, U_ZERO_SEED >> 32])
+    assert o[U_ZERO_INDEX & 3] >> 8 == 0
+    assert oracle.uniform(U_ZERO_SEED, U_ZERO_INDEX) == 0.0
+    base = U_ZERO_INDEX - U_ZERO_INDEX % 8
+    g = np.full(8, 0.5, np.float32)                  # d = 4: norm 1, x = 0.5 * 4 = 2
+    nib = oracle.qsgd_levels(g, 4, 4, U_ZERO_SEED, np.ones(2, np.float32), index_base=base)
+    assert list(_nibbles(nib, 8) & 7) == [2] * 8
