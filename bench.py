@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the gradient-compression hot path on one MI355X.
+
+One step = one pass of every hot-path operation over one batch: the 1G
+float32 gradient of the fused-bucket workload (2^30 elements, 128 fusion
+buckets of 8,388,608, t = 1e-3):
+  1. gc2_quantize_buckets   -- 2-bit quantize + residual, one fused launch
+  2. gc2_dequant_reduce     -- sum of W = 16 workers' packed buffers (this
+                               step's words are worker 0; 15 more are
+                               synthetic buffers with i.i.d. codes)
+  3. qsgd_quantize          -- bucketed QSGD, d = 512, s = 7 (per-step seed)
+  4. qsgd_dequant
+Inputs are generated on the device before the timed region (seeded torch
+RNG); a new gradient per step, cycling through up to four buffers.
+
+Prints ONE JSON line.  `value` is whole-step throughput in elements of the
+batch per second; `ops` breaks each operation down (elements/s, GB/s of
+algorithmic traffic, fraction of the 8 TB/s HBM peak); `roofline` is the
+dominant kernel (the fused 2-bit quantizer) timed with HIP events on the
+stream it is launched on; `cpu_baseline` is the CPU oracle on a bounded
+sample of the same workload, single-threaded on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gc2_quantize elements/s and achieved HBM GB/s (% of peak) at 1G fp32 elems"
+HBM_PEAK_GBPS = 8000.0
+W_WORKERS = 16
+QSGD_D, QSGD_S = 512, 7
+# algorithmic HBM bytes per element of each operation
+BYTES = {
+    "gc2_quantize_buckets": 12.25,                         # g, r in; r, 1/4 B of codes out
+    "gc2_dequant_reduce": W_WORKERS * 0.25 + 4.0,          # 16 x 1/4 B in, 4 B out
+    "qsgd_quantize": 4.0 + 0.5 + 4.0 / QSGD_D,             # g in; nibble + norm share out
+    "qsgd_dequant": 0.5 + 4.0 / QSGD_D + 4.0,              # nibble + norm share in; 4 B out
+}
+OPS = list(BYTES)
+PMC_FILE = os.path.join(ROOT, "profiles", "gc2_quantize_buckets_1G_hbm_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "gradient_compression_distributed_amd", "csrc",
+                          "gcq_kernels.hip")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused quantizer from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU work of the oracle sample")
+    p.add_argument("--no-per-bucket", action="store_true",
+                   help="skip the 128-launch comparison of the fused quantizer")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 4 GiB device copy (reference kernel for counters)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: the W workers of the reduce are simulated buffers on one GPU and "
+              "this build runs no collectives.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gradient_compression_distributed_amd as gcq
+    from gradient_compression_distributed_amd import workloads as wl
+
+    gcq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = wl.CONFIGS[5]
+    n, nb, blk = cfg.n, cfg.n // cfg.block, cfg.block
+    K, Wm = args.steps, args.warmup
+
+    # ---------------------------------------------------------- setup (untimed)
+    ngrad = min(K + Wm, 4)
+    grads = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(ngrad)]
+    for i, g in enumerate(grads):
+        wl.fill_bucketed_normal_(g, cfg, i)
+    r = torch.zeros(n, dtype=torch.float32, device=dev)
+    nw = n // 16
+    words = [torch.empty(nw, dtype=torch.int32, device=dev) for _ in range(W_WORKERS)]
+    for w in range(1, W_WORKERS):
+        wl.fill_iid_field_words_(words[w], cfg.cid, w)
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    norms = torch.empty(gcq.qsgd_num_buckets(n, QSGD_D), dtype=torch.float32, device=dev)
+    nib = torch.empty(gcq.qsgd_nibble_words(n), dtype=torch.int32, device=dev)
+    qout = torch.empty(n, dtype=torch.float32, device=dev)
+    wpb = blk // 16
+    blists = [gcq.BucketList([(g[b * blk:(b + 1) * blk], r[b * blk:(b + 1) * blk],
+                               words[0][b * wpb:(b + 1) * wpb], cfg.t) for b in range(nb)])
+              for g in grads]
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)]
+          for _ in range(K)]
+
+    def step(i, events=None):
+        g = grads[i % ngrad]
+        if events:
+            events[0].record()
+        gcq.gc2_quantize_buckets(blists[i % ngrad])
+        if events:
+            events[1].record()
+        gcq.gc2_dequant_reduce(words, n, cfg.t, acc=acc)
+        if events:
+            events[2].record()
+        gcq.qsgd_quantize(g, QSGD_D, QSGD_S, wl.qsgd_seed(i), norms=norms, nibbles=nib)
+        if events:
+            events[3].record()
+        gcq.qsgd_dequant(norms, nib, n, QSGD_D, QSGD_S, out=qout)
+        if events:
+            events[4].record()
+
+    for i in range(Wm):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------- timed region
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(Wm + k, ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    op_ms = {op: sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(K)) / K
+             for j, op in enumerate(OPS)}
+    ops = {}
+    for op in OPS:
+        s = op_ms[op] / 1e3
+        gbps = BYTES[op] * n / s / 1e9
+        ops[op] = {"ms": round(op_ms[op], 4), "elements_per_s": n / s,
+                   "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                   "bytes_per_element": BYTES[op]}
+
+    # fused launch vs 128 per-bucket launches of the same quantizer (untimed
+    # by the step clock; events on the same stream)
+    if not args.no_per_bucket:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, K // 2)
+        g = grads[0]
+        e0.record()
+        for _ in range(reps):
+            for b in range(nb):
+                sl = slice(b * blk, (b + 1) * blk)
+                gcq.gc2_quantize(g[sl], r[sl], cfg.t, out=words[0][b * wpb:(b + 1) * wpb])
+        e1.record()
+        torch.cuda.synchronize()
+        per_bucket_ms = e0.elapsed_time(e1) / reps
+        ops["gc2_quantize_buckets"]["per_bucket_launches_ms"] = round(per_bucket_ms, 4)
+        ops["gc2_quantize_buckets"]["fused_speedup"] = round(
+            per_bucket_ms / op_ms["gc2_quantize_buckets"], 3)
+
+    copy_gbps = None
+    if args.copy_calibration:
+        src = grads[0]
+        dst = acc
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * 4 * n / (e0.elapsed_time(e1) / 5 / 1e3) / 1e9
+
+    q_ms = op_ms["gc2_quantize_buckets"]
+    achieved = BYTES["gc2_quantize_buckets"] * n / (q_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(), "kernel": "gc2_quantize_kernel (fused table)",
+                "algorithmic_bytes_per_launch": BYTES["gc2_quantize_buckets"] * n,
+                "avg_launch_ms": round(q_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, cfg, grads[0], words, np, torch, wl)
+
+    line = {
+        "metric": METRIC, "value": n / (ms_per_step / 1e3), "unit": "elements/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded device RNG; per-bucket N(0, sigma_b^2), "
+                "sigma_b log-uniform in [1e-5, 1e-2]; i.i.d. worker codes)",
+        "config": {"workload": "fused-bucket 2-bit quantize + 16-worker dequant-reduce + "
+                               "QSGD d=512 s=7 quantize/dequant over one 1G-element gradient",
+                   "n": n, "buckets": nb, "bucket_elems": blk, "t": cfg.t,
+                   "workers": W_WORKERS, "qsgd_d": QSGD_D, "qsgd_s": QSGD_S},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ops": ops,
+        "gc2_quantize_elements_per_s": ops["gc2_quantize_buckets"]["elements_per_s"],
+        "device_copy_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
+    """The CPU oracle as it stands, one thread pinned to one core, on whole
+    buckets of the same workload until about --cpu-seconds of work."""
+    import oracle
+
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    blk = cfg.block
+    wpb = blk // 16
+    elems = 0
+    total = 0.0
+    per_op = {op: 0.0 for op in OPS}
+    b = 0
+    while total < args.cpu_seconds and b < cfg.n // blk:
+        g = g_dev[b * blk:(b + 1) * blk].cpu().numpy()
+        ws = [w[b * wpb:(b + 1) * wpb].cpu().numpy().view(np.uint32) for w in words]
+        r = np.zeros(blk, np.float32)
+        t0 = time.perf_counter()
+        ws[0] = oracle.gc2_quantize(g, r, cfg.t)
+        t1 = time.perf_counter()
+        oracle.gc2_dequant_reduce(ws, blk, cfg.t)
+        t2 = time.perf_counter()
+        norms, nib = oracle.qsgd_quantize(g, QSGD_D, QSGD_S, wl.qsgd_seed(0))
+        t3 = time.perf_counter()
+        oracle.qsgd_dequant(norms, nib, blk, QSGD_D, QSGD_S)
+        t4 = time.perf_counter()
+        for op, dt in zip(OPS, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+            per_op[op] += dt
+        total += t4 - t0
+        elems += blk
+        b += 1
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": elems / total, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{b} of {cfg.n // blk} buckets ({elems} elements) of the same step: "
+                      "all four operations, single thread pinned to one core",
+            "seconds": round(total, 3),
+            "ops_elements_per_s": {op: elems / s for op, s in per_op.items()},
+            "host_cpus": os.cpu_count(), "cpu_model": model}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""MI355X (gfx950) gradient-compression hot path: Python binding.
+
+A thin ctypes layer over ``libgcq.so`` (the C ABI of ``include/gcq.h``).
+Every step of the path runs in the library's HIP kernels; this module only
+checks tensor metadata, passes raw device pointers and the current HIP
+stream, and turns a negative status into ``GcqError``.  PyTorch supplies
+device memory and streams.  There is no CPU fallback: if the library is
+missing, ``load()`` raises.
+
+Packed words (2-bit codes, QSGD nibbles) are held in ``torch.int32``
+tensors as raw 32-bit patterns (view them as uint32 on the host).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GcqError", "load", "lib_path", "gc2_quantize", "gc2_quantize_buckets",
+    "gc2_dequant_reduce", "qsgd_quantize", "qsgd_dequant", "gc2_packed_words",
+    "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "BucketList",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libgcq.so"
+MAX_WORKERS = 64
+
+_lib = None
+
+
+class GcqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.gcq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+class Gc2Bucket(ctypes.Structure):
+    _fields_ = [("g", ctypes.c_void_p), ("r", ctypes.c_void_p), ("out_words", ctypes.c_void_p),
+                ("n", ctypes.c_size_t), ("t", ctypes.c_float)]
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, LIB_NAME)
+
+
+def load():
+    """Load libgcq.so from the package directory (raises if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(path)
+    vp, sz, u32, u64, f32, i32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32,
+                                  ctypes.c_uint64, ctypes.c_float, ctypes.c_int)
+    lib.gc2_quantize.argtypes = [vp, vp, sz, f32, vp, vp]
+    lib.gc2_quantize.restype = i32
+    lib.gc2_quantize_buckets.argtypes = [ctypes.POINTER(Gc2Bucket), u32, vp]
+    lib.gc2_quantize_buckets.restype = i32
+    lib.gc2_dequant_reduce.argtypes = [ctypes.POINTER(vp), u32, sz, f32, vp, vp]
+    lib.gc2_dequant_reduce.restype = i32
+    lib.qsgd_quantize.argtypes = [vp, sz, u32, u32, u64, vp, vp, vp]
+    lib.qsgd_quantize.restype = i32
+    lib.qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp, vp]
+    lib.qsgd_dequant.restype = i32
+    lib.gc2_packed_words.argtypes = [sz]
+    lib.gc2_packed_words.restype = sz
+    lib.qsgd_num_buckets.argtypes = [sz, u32]
+    lib.qsgd_num_buckets.restype = sz
+    lib.qsgd_nibble_words.argtypes = [sz]
+    lib.qsgd_nibble_words.restype = sz
+    lib.gcq_status_string.argtypes = [i32]
+    lib.gcq_status_string.restype = ctypes.c_char_p
+    lib.gcq_set_tuning.argtypes = [i32, i32, i32, i32]
+    lib.gcq_set_tuning.restype = i32
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- helpers
+def gc2_packed_words(n: int) -> int:
+    return int(load().gc2_packed_words(n))
+
+
+def qsgd_num_buckets(n: int, d: int) -> int:
+    return int(load().qsgd_num_buckets(n, d))
+
+
+def qsgd_nibble_words(n: int) -> int:
+    return int(load().qsgd_nibble_words(n))
+
+
+def _dev(x, dtype, name, min_numel=0):
+    import torch
+
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory (got {x.device})")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {x.dtype})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if x.numel() < min_numel:
+        raise ValueError(f"{name} holds {x.numel()} elements, needs {min_numel}")
+    return x
+
+
+def _ptr(x):
+    return ctypes.c_void_p(x.data_ptr() if x is not None and x.numel() else 0)
+
+
+def _stream(device=None):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GcqError(status, where)
+
+
+def set_tuning(gc2_layout: int = -1, nt: int = -1, blocks_per_cu: int = -1,
+               dq_blocks_per_cu: int = -1):
+    """Launch knobs (speed only; results are identical); -1 keeps a knob."""
+    _check(load().gcq_set_tuning(gc2_layout, nt, blocks_per_cu, dq_blocks_per_cu),
+           "gcq_set_tuning")
+
+
+# -------------------------------------------------------------- the calls
+def gc2_quantize(g, r, t: float, out=None):
+    """One 2-bit quantize step: returns the packed words, updates ``r``."""
+    import torch
+
+    lib = load()
+    _dev(g, torch.float32, "g")
+    n = g.numel()
+    _dev(r, torch.float32, "r", n)
+    if out is None:
+        out = torch.empty(gc2_packed_words(n), dtype=torch.int32, device=g.device)
+    _dev(out, torch.int32, "out", gc2_packed_words(n))
+    _check(lib.gc2_quantize(_ptr(g), _ptr(r), n, ctypes.c_float(t), _ptr(out),
+                            _stream(g.device)), "gc2_quantize")
+    return out
+
+
+class BucketList:
+    """A checked, reusable descriptor array for gc2_quantize_buckets.
+
+    Holds references to the tensors so their memory outlives the list;
+    building it once and reusing it every step keeps per-call host work to
+    the library's own checks and one launch."""
+
+    def __init__(self, buckets):
+        import torch
+
+        self.tensors = list(buckets)
+        self.array = (Gc2Bucket * max(len(buckets), 1))()
+        self.device = None
+        for i, (g, r, out, t) in enumerate(buckets):
+            _dev(g, torch.float32, f"buckets[{i}].g")
+            n = g.numel()
+            _dev(r, torch.float32, f"buckets[{i}].r", n)
+            _dev(out, torch.int32, f"buckets[{i}].out", gc2_packed_words(n))
+            self.array[i] = Gc2Bucket(g.data_ptr() if n else 0, r.data_ptr() if n else 0,
+                                      out.data_ptr() if n else 0, n, t)
+            self.device = self.device or g.device
+        self.count = len(buckets)
+
+
+def gc2_quantize_buckets(buckets):
+    """Fused launch over ``[(g, r, out, t), ...]`` (or a ``BucketList``);
+    each bucket is quantized exactly as gc2_quantize would."""
+    lib = load()
+    bl = buckets if isinstance(buckets, BucketList) else BucketList(buckets)
+    _check(lib.gc2_quantize_buckets(bl.array, bl.count, _stream(bl.device)),
+           "gc2_quantize_buckets")
+
+
+def gc2_dequant_reduce(words, n: int, t: float, acc=None):
+    """acc = sum over workers 0..W-1 (in order) of the dequantized codes."""
+    import torch
+
+    lib = load()
+    W = len(words)
+    nw = gc2_packed_words(n)
+    for i, w in enumerate(words):
+        _dev(w, torch.int32, f"words[{i}]", nw)
+    if acc is None:
+        acc = torch.empty(n, dtype=torch.float32, device=words[0].device)
+    _dev(acc, torch.float32, "acc", n)
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[w.data_ptr() for w in words])
+    _check(lib.gc2_dequant_reduce(ptrs, W, n, ctypes.c_float(t), _ptr(acc),
+                                  _stream(acc.device)), "gc2_dequant_reduce")
+    return acc
+
+
+def qsgd_quantize(g, d: int, s: int, seed: int, norms=None, nibbles=None):
+    """Bucketed QSGD: returns (norms float32[ceil(n/d)], nibbles int32[ceil(n/8)])."""
+    import torch
+
+    lib = load()
+    _dev(g, torch.float32, "g")
+    n = g.numel()
+    nb, nw = qsgd_num_buckets(n, d), qsgd_nibble_words(n)
+    if norms is None:
+        norms = torch.empty(nb, dtype=torch.float32, device=g.device)
+    if nibbles is None:
+        nibbles = torch.empty(nw, dtype=torch.int32, device=g.device)
+    _dev(norms, torch.float32, "norms", nb)
+    _dev(nibbles, torch.int32, "nibbles", nw)
+    _check(lib.qsgd_quantize(_ptr(g), n, d, s, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+                             _ptr(norms), _ptr(nibbles), _stream(g.device)), "qsgd_quantize")
+    return norms, nibbles
+
+
+def qsgd_dequant(norms, nibbles, n: int, d: int, s: int, out=None):
+    """out = +-(norm * level) / s per element."""
+    import torch
+
+    lib = load()
+    _dev(norms, torch.float32, "norms", qsgd_num_buckets(n, d))
+    _dev(nibbles, torch.int32, "nibbles", qsgd_nibble_words(n))
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=norms.device)
+    _dev(out, torch.float32, "out", n)
+    _check(lib.qsgd_dequant(_ptr(norms), _ptr(nibbles), n, d, s, _ptr(out),
+                            _stream(out.device)), "qsgd_dequant")
+    return out

@@ -1,0 +1,45 @@
+"""Build libgcq.so (the HIP library behind include/gcq.h) for gfx950, in-tree.
+
+Flags: -O3; -ffp-contract=off (no silent a*b+c fusion: results must match
+the plain float32 definition); packed-FP32 instructions disabled in device
+code; no fast-math (denormals kept, IEEE division and square root)."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libgcq.so")
+SOURCES = [os.path.join(CSRC, "gcq_kernels.hip"), os.path.join(CSRC, "gcq_api.hip")]
+ARCH = os.environ.get("GCQ_OFFLOAD_ARCH", "gfx950")
+
+HIPFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", *HIPFLAGS, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-FP32 device feature and says so
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

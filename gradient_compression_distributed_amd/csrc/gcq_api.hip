@@ -1,0 +1,315 @@
+// gcq_api.hip -- the C ABI of libgcq.so (declared and documented in
+// include/gcq.h): host-side argument checks, launch geometry, and the
+// stream-ordered device table of the fused multi-bucket launch.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "gcq.h"
+#include "gcq_internal.h"
+
+namespace {
+
+using gcq::Gc2Desc;
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+    bool writable;
+};
+
+Range range(const void *p, size_t bytes, bool writable)
+{
+    return Range{(uintptr_t)p, (uintptr_t)p + bytes, writable};
+}
+
+// True when a writable range intersects any other range.  Sorted sweep:
+// a pair (A before B in start order) overlaps iff B.lo < A.hi, so it is
+// enough to track the largest end so far among writable and among all
+// ranges.  Read-only ranges may overlap one another.
+bool any_write_overlap(std::vector<Range> &rs)
+{
+    std::sort(rs.begin(), rs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    uintptr_t end_all = 0, end_w = 0;
+    for (const Range &r : rs) {
+        if (r.hi == r.lo)
+            continue;
+        if (r.lo < end_w || (r.writable && r.lo < end_all))
+            return true;
+        end_all = std::max(end_all, r.hi);
+        if (r.writable)
+            end_w = std::max(end_w, r.hi);
+    }
+    return false;
+}
+
+bool valid_threshold(float t) { return isfinite(t) && t > 0.0f; }
+
+constexpr size_t kMaxElems = ((size_t)1 << 62);  // keeps every byte count in range
+
+int check_gc2(const float *g, const float *r, size_t n, float t, const uint32_t *out,
+              std::vector<Range> *ranges)
+{
+    if (!valid_threshold(t))
+        return GCQ_ERR_THRESHOLD;
+    if (n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!g || !r || !out)
+        return GCQ_ERR_NULL;
+    if (!aligned(g, 16) || !aligned(r, 16) || !aligned(out, 4))
+        return GCQ_ERR_ALIGN;
+    ranges->push_back(range(g, n * 4, false));
+    ranges->push_back(range(r, n * 4, true));
+    ranges->push_back(range(out, gc2_packed_words(n) * 4, true));
+    return GCQ_OK;
+}
+
+int launch_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return GCQ_OK;
+    if (e == hipErrorOutOfMemory)
+        return GCQ_ERR_NOMEM;
+    return GCQ_ERR_LAUNCH;
+}
+
+// Device tables of the fused launch: per device a ring of slots, each a
+// pinned host staging buffer, a device buffer and an event recorded after
+// the kernel that reads it.  A slot is reused only once its event has
+// completed, so a call never overwrites a table still in use; the copy and
+// the kernel are ordered on the caller's stream.
+constexpr int kRing = 8;
+constexpr int kMaxDevices = 64;
+
+struct Slot {
+    Gc2Desc *host = nullptr;
+    Gc2Desc *dev = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+
+struct DeviceRing {
+    std::mutex mu;
+    Slot slots[kRing];
+    unsigned next = 0;
+};
+
+DeviceRing g_rings[kMaxDevices];
+
+int ensure_capacity(Slot &s, size_t nb)
+{
+    if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
+        return GCQ_ERR_NOMEM;
+    if (s.cap >= nb)
+        return GCQ_OK;
+    size_t cap = std::max<size_t>(nb, 2 * s.cap);
+    if (s.host)
+        (void)hipHostFree(s.host);
+    if (s.dev)
+        (void)hipFree(s.dev);
+    s.host = nullptr;
+    s.dev = nullptr;
+    s.cap = 0;
+    if (hipHostMalloc((void **)&s.host, cap * sizeof(Gc2Desc), hipHostMallocDefault) != hipSuccess)
+        return GCQ_ERR_NOMEM;
+    if (hipMalloc((void **)&s.dev, cap * sizeof(Gc2Desc)) != hipSuccess) {
+        (void)hipHostFree(s.host);
+        s.host = nullptr;
+        return GCQ_ERR_NOMEM;
+    }
+    s.cap = cap;
+    return GCQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gc2_packed_words(size_t n) { return n / 16 + (n % 16 != 0); }
+
+size_t qsgd_num_buckets(size_t n, uint32_t d) { return d ? n / d + (n % d != 0) : 0; }
+
+size_t qsgd_nibble_words(size_t n) { return n / 8 + (n % 8 != 0); }
+
+const char *gcq_status_string(int status)
+{
+    switch (status) {
+    case GCQ_OK: return "ok";
+    case GCQ_ERR_NULL: return "null pointer with n > 0";
+    case GCQ_ERR_THRESHOLD: return "threshold must be finite and > 0";
+    case GCQ_ERR_PARAM: return "parameter out of range";
+    case GCQ_ERR_ALIGN: return "pointer misaligned (float arrays 16 B, word arrays 4 B)";
+    case GCQ_ERR_OVERLAP: return "an output range overlaps another operand";
+    case GCQ_ERR_LAUNCH: return "HIP launch or copy failed";
+    case GCQ_ERR_NOMEM: return "could not allocate a library buffer";
+    default: return "unknown status";
+    }
+}
+
+int gcq_set_tuning(int gc2_layout, int nt, int blocks_per_cu, int dq_blocks_per_cu)
+{
+    if (gc2_layout > 1 || nt > 1 || blocks_per_cu > 1024 || dq_blocks_per_cu > 1024)
+        return GCQ_ERR_PARAM;
+    gcq::Tuning t = gcq::tuning();
+    if (gc2_layout >= 0)
+        t.gc2_layout = gc2_layout;
+    if (nt >= 0)
+        t.nt = nt;
+    if (blocks_per_cu >= 0)
+        t.blocks_per_cu = blocks_per_cu;
+    if (dq_blocks_per_cu >= 0)
+        t.dq_blocks_per_cu = dq_blocks_per_cu;
+    gcq::set_tuning(t);
+    return GCQ_OK;
+}
+
+int gc2_quantize(const float *g, float *r, size_t n, float t, uint32_t *out_words, void *stream)
+{
+    std::vector<Range> ranges;
+    int st = check_gc2(g, r, n, t, out_words, &ranges);
+    if (st != GCQ_OK || n == 0)
+        return st;
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    Gc2Desc d = {g, r, out_words, (uint64_t)n, 0, t, 0};
+    return launch_status(gcq::launch_gc2_single(d, (hipStream_t)stream));
+}
+
+int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *stream)
+{
+    if (num_buckets == 0)
+        return GCQ_OK;
+    if (!buckets)
+        return GCQ_ERR_NULL;
+    if (num_buckets > 0x7FFFFFFFu)
+        return GCQ_ERR_PARAM;
+    std::vector<Range> ranges;
+    ranges.reserve(3 * (size_t)num_buckets);
+    uint64_t total_tiles = 0;
+    for (uint32_t b = 0; b < num_buckets; ++b) {
+        const gc2_bucket &k = buckets[b];
+        int st = check_gc2(k.g, k.r, k.n, k.t, k.out_words, &ranges);
+        if (st != GCQ_OK)
+            return st;
+        total_tiles += (k.n + gcq::kTileElems - 1) / gcq::kTileElems;
+    }
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    if (total_tiles == 0)
+        return GCQ_OK;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GCQ_ERR_LAUNCH;
+    DeviceRing &ring = g_rings[dev];
+    std::lock_guard<std::mutex> lock(ring.mu);
+    Slot &s = ring.slots[ring.next++ % kRing];
+    if (s.pending) {
+        if (hipEventSynchronize(s.ev) != hipSuccess)
+            return GCQ_ERR_LAUNCH;
+        s.pending = false;
+    }
+    int st = ensure_capacity(s, num_buckets);
+    if (st != GCQ_OK)
+        return st;
+    uint64_t tile = 0;
+    for (uint32_t b = 0; b < num_buckets; ++b) {
+        const gc2_bucket &k = buckets[b];
+        s.host[b] = Gc2Desc{k.g, k.r, k.out_words, (uint64_t)k.n, tile, k.t, 0};
+        tile += (k.n + gcq::kTileElems - 1) / gcq::kTileElems;
+    }
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(s.dev, s.host, num_buckets * sizeof(Gc2Desc),
+                                  hipMemcpyHostToDevice, hs);
+    if (e != hipSuccess)
+        return GCQ_ERR_LAUNCH;
+    e = gcq::launch_gc2_table(s.dev, num_buckets, total_tiles, hs);
+    if (e != hipSuccess)
+        return launch_status(e);
+    if (hipEventRecord(s.ev, hs) != hipSuccess)
+        return GCQ_ERR_LAUNCH;
+    s.pending = true;
+    return GCQ_OK;
+}
+
+int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t, float *acc,
+                       void *stream)
+{
+    if (W == 0 || W > GCQ_MAX_WORKERS)
+        return GCQ_ERR_PARAM;
+    if (!valid_threshold(t))
+        return GCQ_ERR_THRESHOLD;
+    if (n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!words || !acc)
+        return GCQ_ERR_NULL;
+    gcq::DqWorkers ws;
+    memset(&ws, 0, sizeof ws);
+    std::vector<Range> ranges;
+    const size_t wbytes = gc2_packed_words(n) * 4;
+    for (uint32_t w = 0; w < W; ++w) {
+        if (!words[w])
+            return GCQ_ERR_NULL;
+        if (!aligned(words[w], 4))
+            return GCQ_ERR_ALIGN;
+        ws.w[w] = words[w];
+        ranges.push_back(range(words[w], wbytes, false));
+    }
+    if (!aligned(acc, 16))
+        return GCQ_ERR_ALIGN;
+    ranges.push_back(range(acc, n * 4, true));
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(gcq::launch_dequant_reduce(ws, W, n, t, acc, (hipStream_t)stream));
+}
+
+int qsgd_quantize(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed, float *norms,
+                  uint32_t *nibbles, void *stream)
+{
+    if (d == 0 || s < 1 || s > 7 || n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!g || !norms || !nibbles)
+        return GCQ_ERR_NULL;
+    if (!aligned(g, 16) || !aligned(norms, 4) || !aligned(nibbles, 4))
+        return GCQ_ERR_ALIGN;
+    std::vector<Range> ranges = {range(g, n * 4, false),
+                                 range(norms, qsgd_num_buckets(n, d) * 4, true),
+                                 range(nibbles, qsgd_nibble_words(n) * 4, true)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(
+        gcq::launch_qsgd_quantize(g, n, d, s, seed, norms, nibbles, (hipStream_t)stream));
+}
+
+int qsgd_dequant(const float *norms, const uint32_t *nibbles, size_t n, uint32_t d, uint32_t s,
+                 float *out, void *stream)
+{
+    if (d == 0 || s < 1 || s > 7 || n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!norms || !nibbles || !out)
+        return GCQ_ERR_NULL;
+    if (!aligned(norms, 4) || !aligned(nibbles, 4) || !aligned(out, 16))
+        return GCQ_ERR_ALIGN;
+    std::vector<Range> ranges = {range(norms, qsgd_num_buckets(n, d) * 4, false),
+                                 range(nibbles, qsgd_nibble_words(n) * 4, false),
+                                 range(out, n * 4, true)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(
+        gcq::launch_qsgd_dequant(norms, nibbles, n, d, s, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -102,18 +102,22 @@ def gradient_block(cfg: Config, step: int, b: int) -> np.ndarray:
 def iid_field_words(gen: np.random.Generator, nwords: int, p11: float = 0.05,
                     p10: float = 0.05) -> np.ndarray:
     """Random 32-bit words whose sixteen 2-bit fields are i.i.d.:
-    0b11 with probability p11, 0b10 with p10, else 0b00.
+    0b11 with probability p11, 0b10 with p10, else 0b00 (probabilities
+    rounded to multiples of 2^-16).
 
     Fields are independent and identically distributed, so which field goes
     to which bit pair does not matter; field k is put at bits 2k..2k+1."""
-    out = np.zeros(nwords, dtype=np.uint32)
+    c11 = int(round(p11 * 65536))
+    c10 = int(round((p11 + p10) * 65536))
+    out = np.empty(nwords, dtype=np.uint32)
     chunk = 1 << 20
     for lo in range(0, nwords, chunk):
         hi = min(lo + chunk, nwords)
-        u = gen.random((hi - lo, 16), dtype=np.float32)
-        f = np.where(u < p11, 3, np.where(u < p11 + p10, 2, 0)).astype(np.uint32)
-        f <<= (2 * np.arange(16, dtype=np.uint32))[None, :]
-        out[lo:hi] = np.bitwise_or.reduce(f, axis=1)
+        u = gen.integers(0, 65536, size=(hi - lo) * 16, dtype=np.uint16)
+        f = ((u < c10).astype(np.uint8) << 1) | (u < c11).astype(np.uint8)
+        f = f.reshape(hi - lo, 4, 4)
+        byte = f[:, :, 0] | (f[:, :, 1] << 2) | (f[:, :, 2] << 4) | (f[:, :, 3] << 6)
+        out[lo:hi] = np.ascontiguousarray(byte).view("<u4").ravel()
     return out
 
 

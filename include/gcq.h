@@ -1,0 +1,242 @@
+/*
+ * gcq.h -- C ABI of the MI355X (gfx950) gradient-compression library
+ * (libgcq.so).
+ *
+ * The calls follow the statement of the problem on these pages:
+ *   - apache/mxnet pull request "2bit gradient compression": sections "Two
+ *     bit quantization", "Format of compressed gradient", "Local kvstore",
+ *     "Dist kvstore", and the review thread (no default threshold; a new
+ *     threshold takes effect on later calls).
+ *   - "CD-SGD: Distributed Stochastic Gradient Descent with Compression and
+ *     Delay Compensation": 3.4.1 "Update Rules" (a code that passes the
+ *     threshold is worth the threshold itself).
+ *   - "QSGD: Communication-Efficient SGD via Gradient Quantization and
+ *     Encoding" (chapterpal summary): Knowl 1 (Q_s), Knowl 2 (the
+ *     (norm, sign, level) tuple), Knowl 3 (encode, broadcast, decode),
+ *     Knowl 8 (bucketing).
+ *   - blog "IMerge修改（Design）": consecutive layers merged into
+ *     transmission units (fusion buckets), one unit per message.
+ *
+ * Conventions shared by every call:
+ *   - Array pointers are DEVICE pointers (HIP device memory, e.g. torch
+ *     tensors on a ROCm device) owned by the caller; the library keeps no
+ *     reference to them after the call.  Host arrays are marked "host".
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues work on that stream and returns; it never
+ *     synchronizes.  Faults during execution surface at the caller's next
+ *     synchronization with the stream.
+ *   - Every argument is checked on the host before anything is enqueued; a
+ *     call that returns an error has enqueued nothing and changed nothing.
+ *   - Return value: GCQ_OK (0) or a negative GCQ_ERR_* status;
+ *     gcq_status_string() names it.
+ *   - n == 0 (or W == 0 buckets of work) is a successful no-op.
+ *   - Arithmetic is IEEE float32 with round-to-nearest-even, denormals kept,
+ *     no contraction into fused multiply-add where it would change a result.
+ */
+#ifndef GCQ_H
+#define GCQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gcq_status {
+    GCQ_OK = 0,
+    GCQ_ERR_NULL = -1,      /* a required pointer is NULL while n > 0 */
+    GCQ_ERR_THRESHOLD = -2, /* threshold t is not finite or t <= 0 */
+    GCQ_ERR_PARAM = -3,     /* s, d, W or a bucket count out of range */
+    GCQ_ERR_ALIGN = -4,     /* a pointer is not aligned as documented */
+    GCQ_ERR_OVERLAP = -5,   /* an output range intersects another operand */
+    GCQ_ERR_LAUNCH = -6,    /* the HIP runtime rejected a launch or copy */
+    GCQ_ERR_NOMEM = -7      /* a library-owned buffer could not be grown */
+};
+
+/* Largest W accepted by gc2_dequant_reduce. */
+#define GCQ_MAX_WORKERS 64
+
+/* ------------------------------------------------------------------ */
+/* 2-bit threshold quantizer with error-feedback residual              */
+/* ------------------------------------------------------------------ */
+
+/*
+ * gc2_quantize -- one quantization step of the MXNet PR's 2-bit scheme
+ * ("Two bit quantization", "Format of compressed gradient"), with the
+ * residual of CD-SGD 3.4.1.
+ *
+ * For every i < n, in float32:
+ *     v = g[i] + r[i]
+ *     code = 11 if v >= t, 10 if v <= -t, else 00
+ *     r[i] = v - (+t | -t | +0)          (the value the code stands for)
+ * and code i is written to bits [31-2(i%16) : 30-2(i%16)] of
+ * out_words[i/16], i.e. 16 codes per 32-bit word, first element in the most
+ * significant bit pair; pairs past n in the last word are 00.
+ *
+ *   g          in,     float32[n], 16-byte aligned
+ *   r          in/out, float32[n], 16-byte aligned; the residual carried
+ *              between steps (the only state of the method)
+ *   n          element count (any value, including a ragged tail)
+ *   t          threshold, finite and > 0 (there is no default)
+ *   out_words  out,    uint32[ceil(n/16)], 4-byte aligned, overwritten
+ *   stream     hipStream_t
+ *
+ * Errors: GCQ_ERR_NULL, GCQ_ERR_THRESHOLD, GCQ_ERR_ALIGN, GCQ_ERR_OVERLAP
+ * (g, r and out_words must be pairwise disjoint), GCQ_ERR_LAUNCH.
+ */
+int gc2_quantize(const float *g, float *r, size_t n, float t, uint32_t *out_words,
+                 void *stream);
+
+/* One fusion bucket: its own gradient, residual, packed output and
+ * threshold.  Field meaning and alignment as in gc2_quantize. */
+typedef struct gc2_bucket {
+    const float *g;
+    float *r;
+    uint32_t *out_words;
+    size_t n;
+    float t;
+} gc2_bucket;
+
+/*
+ * gc2_quantize_buckets -- gc2_quantize applied to each of num_buckets
+ * buckets in ONE kernel launch (IMerge-style merged transmission units).
+ * Each bucket is quantized exactly as gc2_quantize would quantize it alone:
+ * its packing starts at its own out_words[0], its tail pairs are 00.
+ *
+ *   buckets      host array of num_buckets descriptors; read during the
+ *                call only (the library copies it into a library-owned,
+ *                stream-ordered device table, grown on demand)
+ *   num_buckets  0 .. 2^31-1
+ *   stream       hipStream_t
+ *
+ * Errors: as gc2_quantize for any bucket (nothing is launched if one bucket
+ * is invalid); GCQ_ERR_OVERLAP also when two buckets' writable ranges (r,
+ * out_words) intersect each other or another bucket's g; GCQ_ERR_NOMEM.
+ */
+int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *stream);
+
+/*
+ * gc2_dequant_reduce -- the receiving side of the MXNet PR's "Local
+ * kvstore" (device 0 dequantizes every device's packed gradient and sums
+ * them) and "Dist kvstore" (the server dequantizes to full size).  With
+ * code(w, i) read as in gc2_quantize and 11 -> +t, 10 -> -t, 00 and 01 -> 0:
+ *     acc[i] = ((+0 + val(0, i)) + val(1, i)) + ... + val(W-1, i)
+ * in float32, workers added in the order 0, 1, ..., W-1 (the order fixes
+ * the rounding; the result is bit-exact with that sequential sum).
+ *
+ *   words   host array of W device pointers, each uint32[ceil(n/16)],
+ *           4-byte aligned, read only (they may alias one another)
+ *   W       1 .. GCQ_MAX_WORKERS
+ *   n       element count
+ *   t       threshold the codes were made with, finite and > 0
+ *   acc     out, float32[n], 16-byte aligned, overwritten (not accumulated)
+ *   stream  hipStream_t
+ *
+ * Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (W), GCQ_ERR_THRESHOLD, GCQ_ERR_ALIGN,
+ * GCQ_ERR_OVERLAP (acc intersects a words buffer), GCQ_ERR_LAUNCH.
+ */
+int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t,
+                       float *acc, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* QSGD: bucketed s-level stochastic quantizer                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * qsgd_quantize -- Q_s of the QSGD summary (Knowl 1) applied per bucket of d
+ * contiguous elements (Knowl 8), each bucket scaled by its own L2 norm; the
+ * output is the (norm, sign, level) tuple of Knowl 2 as fixed-width
+ * nibbles.
+ *
+ * Bucket b covers elements [b*d, min(b*d + d, n)).  norms[b] is its L2
+ * norm, accumulated in float64 and rounded once to float32.  For element i
+ * of bucket b, in float32:
+ *     if norms[b] == 0: level = 0                       (Q_s(0) = 0)
+ *     else: a = |g[i]| / norms[b]  (correctly rounded), x = a * s,
+ *           x >= s -> level s; x NaN -> level 0; otherwise
+ *           l = floor(x), p = x - l, level = l + (u_i < p)
+ *     sign = (g[i] < 0)                                 (sgn(0) = +1)
+ *     nibble = sign << 3 | level, 8 nibbles per uint32 word, first element
+ *     in the most significant nibble, nibbles past n zero.
+ * u_i = (word >> 8) * 2^-24 where word is output word (i % 4) of
+ * Philox-4x32-10 (Salmon et al., SC'11) with counter (i/4 low 32 bits,
+ * i/4 high 32 bits, 0, 0) and key (seed low 32 bits, seed high 32 bits).
+ * u_i depends only on (seed, i), never on how the work is split.
+ *
+ *   g        in,  float32[n], 16-byte aligned
+ *   n        element count
+ *   d        bucket length, >= 1
+ *   s        number of levels, 1 .. 7 (a level must fit in 3 bits)
+ *   seed     64-bit seed of the uniforms (one per step)
+ *   norms    out, float32[ceil(n/d)], 4-byte aligned, overwritten
+ *   nibbles  out, uint32[ceil(n/8)], 4-byte aligned, overwritten
+ *   stream   hipStream_t
+ *
+ * Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (d, s), GCQ_ERR_ALIGN,
+ * GCQ_ERR_OVERLAP (g, norms, nibbles pairwise disjoint), GCQ_ERR_LAUNCH.
+ */
+int qsgd_quantize(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed,
+                  float *norms, uint32_t *nibbles, void *stream);
+
+/*
+ * qsgd_dequant -- "Decode" of the QSGD summary's Knowl 3: with level and
+ * sign read from nibble i as stored (no clamping), in float32:
+ *     out[i] = +-( (norms[i/d] * level) / s )    (- when the sign bit is 1)
+ *
+ *   norms    in,  float32[ceil(n/d)], 4-byte aligned
+ *   nibbles  in,  uint32[ceil(n/8)], 4-byte aligned
+ *   n, d, s  as in qsgd_quantize
+ *   out      out, float32[n], 16-byte aligned, overwritten
+ *   stream   hipStream_t
+ *
+ * Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM, GCQ_ERR_ALIGN, GCQ_ERR_OVERLAP
+ * (out intersects an input), GCQ_ERR_LAUNCH.
+ */
+int qsgd_dequant(const float *norms, const uint32_t *nibbles, size_t n, uint32_t d,
+                 uint32_t s, float *out, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Sizes and status names (pure host functions, no device access)      */
+/* ------------------------------------------------------------------ */
+
+/* ceil(n/16): packed 2-bit words for n elements (MXNet PR: 1/16 the size). */
+size_t gc2_packed_words(size_t n);
+/* ceil(n/d): QSGD buckets (d >= 1; returns 0 for d == 0). */
+size_t qsgd_num_buckets(size_t n, uint32_t d);
+/* ceil(n/8): QSGD nibble words. */
+size_t qsgd_nibble_words(size_t n);
+/* Static, never-NULL name of a status code. */
+const char *gcq_status_string(int status);
+
+/* ------------------------------------------------------------------ */
+/* Launch knobs: they change speed, never results                      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * gcq_set_tuning -- choose how the kernels map work to the GPU.  Every
+ * setting produces bit-identical outputs.
+ *   gc2_layout        0: lanes load 16-byte pieces side by side and each
+ *                        quad of lanes assembles four packed words (default)
+ *                     1: each lane owns a 64-byte run of 16 elements
+ *   nt                1: non-temporal hints on streamed loads and stores
+ *                        (default); 0: ordinary cached accesses
+ *   blocks_per_cu     workgroups per compute unit of the 2-bit quantizer
+ *                     (grid-stride); 0: one 4096-element tile per workgroup
+ *                     (default)
+ *   dq_blocks_per_cu  the same for gc2_dequant_reduce (0: one packed word
+ *                     per thread, default)
+ * A negative argument leaves that knob unchanged.  The initial values come
+ * from the environment variables GCQ_GC2_LAYOUT, GCQ_NT, GCQ_BLOCKS_PER_CU
+ * and GCQ_DQ_BLOCKS_PER_CU.  Takes effect for calls made after it returns;
+ * it must not run concurrently with another call of this library.
+ * Returns GCQ_OK, or GCQ_ERR_PARAM if a value is out of range (layout > 1,
+ * nt > 1, a block count > 1024).
+ */
+int gcq_set_tuning(int gc2_layout, int nt, int blocks_per_cu, int dq_blocks_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCQ_H */

@@ -1,0 +1,124 @@
+"""GPU parity of gc2_dequant_reduce against the CPU oracle, bit-exact.
+
+MXNet PR "2bit gradient compression", "Local kvstore": device 0
+dequantizes the W devices' packed gradients and sums them; CD-SGD 3.4.1:
+11 -> +t, 10 -> -t.  The sum is taken in worker order 0..W-1."""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_compression_distributed_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+def dev(a):
+    import torch
+
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint32) if a.dtype == np.int32 else a
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def test_config3_w16(gpu):
+    cfg = wl.CONFIGS[3]
+    say("dequant config 3", cfg.n, cfg.workers)
+    nw = oracle.packed_words(cfg.n)
+    ws = [wl.worker_words(cfg, w, nw) for w in range(cfg.workers)]
+    acc_d = gpu.gc2_dequant_reduce([dev(w) for w in ws], cfg.n, cfg.t)
+    acc_h = oracle.gc2_dequant_reduce(ws, cfg.n, cfg.t)
+    assert np.array_equal(bits(host(acc_d)), bits(acc_h))
+
+
+@pytest.mark.parametrize("dq_bpc", [0, 4])
+def test_workers_sizes_thresholds(gpu, dq_bpc):
+    import torch
+
+    gpu.set_tuning(dq_blocks_per_cu=dq_bpc)
+    try:
+        rs = np.random.default_rng(21 + dq_bpc)
+        for W in (1, 2, 3, 7, 15, 16, 17, 31, 33, 64):
+            for n in (1, 15, 16, 17, 63, 4095, 4097, 100_003):
+                # t = 1e-37 exercises the path for thresholds below 2^-120
+                t = float(rs.choice([0.01, 1e-3, 0.5, 0.1, 7.7, 1e-37]))
+                say("dequant W", W, "n", n, "t", t)
+                nw = oracle.packed_words(n)
+                ws = [wl.iid_field_words(rs, nw, 0.3, 0.3) for _ in range(W)]
+                # sprinkle the never-produced code 01 (read as zero)
+                ws[0][: max(1, nw // 3)] |= np.uint32(0x11111111)
+                ws[0][: max(1, nw // 3)] &= np.uint32(~0x22222222 & 0xFFFFFFFF)
+                guard = torch.full((n + 64,), 1234.5, device="cuda")
+                gpu.gc2_dequant_reduce([dev(w) for w in ws], n, t, acc=guard[:n])
+                acc_h = oracle.gc2_dequant_reduce(ws, n, t)
+                out = host(guard)
+                assert np.array_equal(bits(out[:n]), bits(acc_h)), (W, n, t)
+                assert np.all(out[n:] == np.float32(1234.5))
+    finally:
+        gpu.set_tuning(dq_blocks_per_cu=0)
+
+
+def test_aliased_workers(gpu):
+    say("dequant aliased workers")
+    n = 10_000
+    w = wl.iid_field_words(np.random.default_rng(4), oracle.packed_words(n), 0.4, 0.4)
+    d = dev(w)
+    acc = gpu.gc2_dequant_reduce([d, d, d, d, d], n, 1e-3)
+    assert np.array_equal(bits(host(acc)), bits(oracle.gc2_dequant_reduce([w] * 5, n, 1e-3)))
+
+
+def test_roundtrip_with_gpu_quantizer(gpu):
+    # W workers quantize their own gradients on the GPU, the reduce sums
+    # them; compared with the oracle doing both steps
+    import torch
+
+    say("dequant roundtrip")
+    n, W, t = 200_001, 8, 0.01
+    rs = np.random.default_rng(12)
+    gs = [(rs.standard_normal(n) * 0.01).astype(np.float32) for _ in range(W)]
+    words_d, words_h = [], []
+    for g in gs:
+        r_d = torch.zeros(n, device="cuda")
+        words_d.append(gpu.gc2_quantize(dev(g), r_d, t))
+        words_h.append(oracle.gc2_quantize(g, np.zeros(n, np.float32), t))
+    acc = gpu.gc2_dequant_reduce(words_d, n, t)
+    assert np.array_equal(bits(host(acc)), bits(oracle.gc2_dequant_reduce(words_h, n, t)))
+
+
+def test_full_size_1g_sampled(gpu):
+    """The benchmark's shape: W = 16 buffers of 2^30 elements (device
+    generated), sampled outputs checked against the oracle one word at a
+    time, plus the exact closed form at a power-of-two threshold on a
+    slice."""
+    import torch
+
+    n, W, t = 1 << 30, 16, 1e-3
+    say("dequant 1G W16")
+    nw = n // 16
+    ws = [torch.empty(nw, dtype=torch.int32, device="cuda") for _ in range(W)]
+    for w in range(W):
+        wl.fill_iid_field_words_(ws[w], 5, w)
+    acc = torch.empty(n, device="cuda")
+    gpu.gc2_dequant_reduce(ws, n, t, acc=acc)
+    torch.cuda.synchronize()
+    say("1G reduce done")
+    rs = np.random.default_rng(77)
+    pos = np.unique(np.concatenate([rs.integers(0, nw, 20_000), [0, nw - 1]]))
+    pos_d = torch.from_numpy(pos).cuda()
+    sampled = [ws[w][pos_d].cpu().numpy().view(np.uint32).copy() for w in range(W)]
+    want = oracle.gc2_dequant_reduce(sampled, pos.size * 16, t)
+    idx = (pos_d.view(-1, 1) * 16 + torch.arange(16, device="cuda").view(1, -1)).view(-1)
+    got = acc[idx].cpu().numpy()
+    assert np.array_equal(bits(got), bits(want))
