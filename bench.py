@@ -46,13 +46,18 @@ BYTES = {
 }
 OPS = list(BYTES)
 PMC_FILE = os.path.join(ROOT, "profiles", "gc2_quantize_buckets_1G_hbm_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "gradient_compression_distributed_amd", "csrc",
-                          "gcq_kernels.hip")
+CSRC = os.path.join(ROOT, "gradient_compression_distributed_amd", "csrc")
+# the fused quantizer's source: the counters are valid only for this text
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gc2_quantize.hip", "gcq_device.h",
+                                               "gcq_internal.h")]
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

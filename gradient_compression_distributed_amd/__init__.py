@@ -18,7 +18,7 @@ import os
 __all__ = [
     "GcqError", "load", "lib_path", "gc2_quantize", "gc2_quantize_buckets",
     "gc2_dequant_reduce", "qsgd_quantize", "qsgd_dequant", "gc2_packed_words",
-    "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "BucketList",
+    "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "get_tuning", "BucketList",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,16 @@ class GcqError(RuntimeError):
         self.status = status
         msg = _lib.gcq_status_string(status).decode() if _lib is not None else str(status)
         super().__init__(f"{where}: status {status} ({msg})")
+
+
+class Tuning(ctypes.Structure):
+    """Mirror of ``gcq_tuning`` (launch knobs; results never depend on them)."""
+    _fields_ = [(f, ctypes.c_int) for f in (
+        "gc2_layout", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
+        "dq_lds_stores", "dq_blocks_per_cu", "qsgd_nt")]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 class Gc2Bucket(ctypes.Structure):
@@ -74,7 +84,9 @@ def load():
     lib.qsgd_nibble_words.restype = sz
     lib.gcq_status_string.argtypes = [i32]
     lib.gcq_status_string.restype = ctypes.c_char_p
-    lib.gcq_set_tuning.argtypes = [i32, i32, i32, i32]
+    lib.gcq_get_tuning.argtypes = [ctypes.POINTER(Tuning)]
+    lib.gcq_get_tuning.restype = i32
+    lib.gcq_set_tuning.argtypes = [ctypes.POINTER(Tuning)]
     lib.gcq_set_tuning.restype = i32
     _lib = lib
     return lib
@@ -124,11 +136,25 @@ def _check(status: int, where: str):
         raise GcqError(status, where)
 
 
-def set_tuning(gc2_layout: int = -1, nt: int = -1, blocks_per_cu: int = -1,
-               dq_blocks_per_cu: int = -1):
-    """Launch knobs (speed only; results are identical); -1 keeps a knob."""
-    _check(load().gcq_set_tuning(gc2_layout, nt, blocks_per_cu, dq_blocks_per_cu),
-           "gcq_set_tuning")
+def get_tuning() -> dict:
+    """Current launch knobs as a dict (see ``gcq_tuning`` in include/gcq.h)."""
+    t = Tuning()
+    _check(load().gcq_get_tuning(ctypes.byref(t)), "gcq_get_tuning")
+    return t.as_dict()
+
+
+def set_tuning(**knobs) -> dict:
+    """Change some launch knobs (speed only; results are identical).
+    Returns the previous settings, so ``set_tuning(**old)`` restores them."""
+    t = Tuning()
+    _check(load().gcq_get_tuning(ctypes.byref(t)), "gcq_get_tuning")
+    old = t.as_dict()
+    for k, v in knobs.items():
+        if k not in old:
+            raise KeyError(f"unknown tuning knob {k!r}")
+        setattr(t, k, int(v))
+    _check(load().gcq_set_tuning(ctypes.byref(t)), "gcq_set_tuning")
+    return old
 
 
 # -------------------------------------------------------------- the calls

@@ -1,0 +1,245 @@
+// gc2_quantize.hip -- the 2-bit threshold quantizer with error-feedback
+// residual (MXNet PR "2bit gradient compression": "Two bit quantization",
+// "Format of compressed gradient"; CD-SGD 3.4.1 "Update Rules") for gfx950,
+// single buffer and fused multi-bucket (IMerge-style merged transmission
+// units) launches.
+//
+// HBM-bound: per element 4 B of g and 4 B of r are read, 4 B of r and 1/4 B
+// of packed code written (12.25 B), ~10 VALU ops of arithmetic.  No MFMA.
+// Float work is IEEE float32 round-to-nearest; the library is built with
+// -ffp-contract=off.
+#include "gcq_device.h"
+#include "gcq_internal.h"
+
+namespace gcq {
+
+namespace {
+
+using dev::ld;
+using dev::st;
+using dev::v4f;
+
+// 11 at or above +t, 10 at or below -t, 00 otherwise (NaN compares false).
+__device__ __forceinline__ uint32_t gc2_code(float v, float t)
+{
+    const uint32_t up = v >= t ? 1u : 0u;
+    const uint32_t dn = v <= -t ? 1u : 0u;
+    return ((up | dn) << 1) | up;
+}
+
+// What is not sent stays in the residual: 11 sends +t, 10 sends -t.
+__device__ __forceinline__ float gc2_residual(float v, uint32_t code, float t)
+{
+    const float sent = code == 3u ? t : (code == 2u ? -t : 0.0f);
+    return v - sent;
+}
+
+// Four elements -> their residuals (stored) and one byte of codes, first
+// element in the top bit pair.
+template <bool NT, typename RP>
+__device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
+{
+    const v4f v = g + r;
+    const uint32_t c0 = gc2_code(v.x, t), c1 = gc2_code(v.y, t);
+    const uint32_t c2 = gc2_code(v.z, t), c3 = gc2_code(v.w, t);
+    v4f rn;
+    rn.x = gc2_residual(v.x, c0, t);
+    rn.y = gc2_residual(v.y, c1, t);
+    rn.z = gc2_residual(v.z, c2, t);
+    rn.w = gc2_residual(v.w, c3, t);
+    st<NT>(rout, rn);
+    return (c0 << 6) | (c1 << 4) | (c2 << 2) | c3;
+}
+
+// Full wave tile, layout 0.  Lane L loads elements 256k + 4L .. +3 of the
+// tile for k = 0..3, so every dwordx4 load of the wave covers 1 KiB of
+// consecutive memory.  Those four elements are byte (L % 4) of packed word
+// 16k + L/4 (byte 0 = most significant).  A quad of lanes therefore holds
+// the four bytes of four words; one DPP broadcast per source lane lets lane
+// 4m + j assemble word 16j + m, so the wave stores its 64 words as one
+// 256-byte block.
+template <bool NT>
+__device__ __forceinline__ void gc2_tile_coalesced(const GCQ_GLOBAL float *__restrict__ g,
+                                                   GCQ_GLOBAL float *__restrict__ r,
+                                                   GCQ_GLOBAL uint32_t *__restrict__ out, float t,
+                                                   uint32_t lane)
+{
+    const GCQ_GLOBAL v4f *g4 = (const GCQ_GLOBAL v4f *)g;
+    GCQ_GLOBAL v4f *r4 = (GCQ_GLOBAL v4f *)r;
+    v4f gv[4], rv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        gv[k] = ld<NT>(g4 + k * kWave + lane);
+        rv[k] = ld<NT>(r4 + k * kWave + lane);
+    }
+    uint32_t bytes = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        bytes |= gc2_quad<NT>(gv[k], rv[k], t, r4 + k * kWave + lane) << (8 * k);
+    const uint32_t x0 = dev::dpp<dev::kQuadBcast0>(bytes), x1 = dev::dpp<dev::kQuadBcast1>(bytes);
+    const uint32_t x2 = dev::dpp<dev::kQuadBcast2>(bytes), x3 = dev::dpp<dev::kQuadBcast3>(bytes);
+    const uint32_t j = lane & 3u, sh = 8u * j;
+    const uint32_t word = (((x0 >> sh) & 0xFFu) << 24) | (((x1 >> sh) & 0xFFu) << 16) |
+                          (((x2 >> sh) & 0xFFu) << 8) | ((x3 >> sh) & 0xFFu);
+    st<NT>(out + 16u * j + (lane >> 2), word);
+}
+
+// Full wave tile, layout 1: lane L owns elements 16L .. 16L+15 (a 64-byte
+// run, four dwordx4 loads 64 bytes apart across lanes) and packs its own
+// word with no cross-lane traffic.
+template <bool NT>
+__device__ __forceinline__ void gc2_tile_runs(const GCQ_GLOBAL float *__restrict__ g,
+                                              GCQ_GLOBAL float *__restrict__ r,
+                                              GCQ_GLOBAL uint32_t *__restrict__ out, float t,
+                                              uint32_t lane)
+{
+    const GCQ_GLOBAL v4f *g4 = (const GCQ_GLOBAL v4f *)g + 4u * lane;
+    GCQ_GLOBAL v4f *r4 = (GCQ_GLOBAL v4f *)r + 4u * lane;
+    v4f gv[4], rv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        gv[k] = ld<NT>(g4 + k);
+        rv[k] = ld<NT>(r4 + k);
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        word |= gc2_quad<NT>(gv[k], rv[k], t, r4 + k) << (24 - 8 * k);
+    st<NT>(out + lane, word);
+}
+
+// Wave tile that runs past the end of its bucket: lane L packs word
+// (e0/16 + L) element by element with bounds checks; pairs past n stay 00.
+__device__ __forceinline__ void gc2_tile_partial(const GCQ_GLOBAL float *__restrict__ g,
+                                                 GCQ_GLOBAL float *__restrict__ r,
+                                                 GCQ_GLOBAL uint32_t *__restrict__ out, uint64_t n,
+                                                 uint64_t e0, float t, uint32_t lane)
+{
+    const uint64_t w = (e0 >> 4) + lane;
+    const uint64_t base = w << 4;
+    if (base >= n)
+        return;
+    uint32_t word = 0;
+    for (uint32_t p = 0; p < 16; ++p) {
+        const uint64_t e = base + p;
+        if (e < n) {
+            const float v = g[e] + r[e];
+            const uint32_t c = gc2_code(v, t);
+            r[e] = gc2_residual(v, c, t);
+            word |= c << (30u - 2u * p);
+        }
+    }
+    out[w] = word;
+}
+
+// Bucket of block tile `tile`: a division when every bucket spans `tpb`
+// tiles, else a binary search for the last bucket whose first tile is
+// <= tile (empty buckets share their successor's first tile and are
+// skipped).  Uniform per workgroup, so it runs on the scalar unit.
+__device__ __forceinline__ uint32_t gc2_find_bucket(const Gc2Desc *__restrict__ table,
+                                                    uint32_t nbuckets, uint64_t tile, uint32_t tpb)
+{
+    if (tpb)
+        return (uint32_t)(tile / tpb);
+    uint32_t lo = 0, hi = nbuckets - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (table[mid].tile_begin <= tile)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// One kernel for the single-buffer call (Table = false: the descriptor is a
+// kernel argument) and the fused multi-bucket call (Table = true: a device
+// table of buckets, each owning a contiguous range of block tiles).  The
+// block -> tile map is a grid-stride loop; with a grid of one block per
+// tile (the default) it runs once.  A block tile is 16 KiB-aligned within
+// its bucket, so no cache line is shared between workgroups, and thus
+// between the XCDs' L2 caches.
+template <int Layout, bool NT, bool Table>
+__global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
+    Gc2Desc one, const Gc2Desc *__restrict__ table, uint32_t nbuckets, uint64_t total_tiles,
+    uint32_t tiles_per_bucket)
+{
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = threadIdx.x / kWave;
+    uint64_t tile = blockIdx.x;
+    if (tile >= total_tiles)
+        return;
+    uint32_t b = 0;
+    if constexpr (Table)
+        b = gc2_find_bucket(table, nbuckets, tile, tiles_per_bucket);
+    for (; tile < total_tiles; tile += gridDim.x) {
+        Gc2Desc d;
+        if constexpr (Table) {
+            if (tiles_per_bucket)
+                b = (uint32_t)(tile / tiles_per_bucket);
+            else
+                while (b + 1 < nbuckets && table[b + 1].tile_begin <= tile)
+                    ++b;
+            d = table[b];
+        } else {
+            d = one;
+        }
+        const GCQ_GLOBAL float *g = (const GCQ_GLOBAL float *)d.g;
+        GCQ_GLOBAL float *r = (GCQ_GLOBAL float *)d.r;
+        GCQ_GLOBAL uint32_t *out = (GCQ_GLOBAL uint32_t *)d.out;
+        const uint64_t e0 = (tile - d.tile_begin) * kTileElems + (uint64_t)wave * kWaveElems;
+        if (e0 + kWaveElems <= d.n) {
+            if constexpr (Layout == 0)
+                gc2_tile_coalesced<NT>(g + e0, r + e0, out + (e0 >> 4), d.t, lane);
+            else
+                gc2_tile_runs<NT>(g + e0, r + e0, out + (e0 >> 4), d.t, lane);
+        } else if (e0 < d.n) {
+            gc2_tile_partial(g, r, out, d.n, e0, d.t, lane);
+        }
+    }
+}
+
+template <bool Table>
+hipError_t launch(const Gc2Desc &one, const Gc2Desc *table, uint32_t nb, uint64_t total_tiles,
+                  uint32_t tpb, hipStream_t stream)
+{
+    const gcq_tuning tu = tuning();
+    const uint32_t grid = grid_for(total_tiles, tu.gc2_blocks_per_cu);
+    const dim3 block(kBlockThreads);
+#define GCQ_GC2(L, NT) \
+    gc2_quantize_kernel<L, NT, Table><<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb)
+    if (tu.gc2_layout == 0) {
+        if (tu.gc2_nt)
+            GCQ_GC2(0, true);
+        else
+            GCQ_GC2(0, false);
+    } else {
+        if (tu.gc2_nt)
+            GCQ_GC2(1, true);
+        else
+            GCQ_GC2(1, false);
+    }
+#undef GCQ_GC2
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream)
+{
+    const uint64_t tiles = (one.n + kTileElems - 1) / kTileElems;
+    if (!tiles)
+        return hipSuccess;
+    return launch<false>(one, nullptr, 1, tiles, 0, stream);
+}
+
+hipError_t launch_gc2_table(const Gc2Desc *dev_table, uint32_t nbuckets, uint64_t total_tiles,
+                            uint32_t tiles_per_bucket, hipStream_t stream)
+{
+    if (!total_tiles || !nbuckets)
+        return hipSuccess;
+    Gc2Desc none = {};
+    return launch<true>(none, dev_table, nbuckets, total_tiles, tiles_per_bucket, stream);
+}
+
+}  // namespace gcq

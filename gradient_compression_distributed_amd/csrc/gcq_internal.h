@@ -1,11 +1,12 @@
-// gcq_internal.h -- declarations shared by the kernels (gcq_kernels.hip) and
-// the C ABI (gcq_api.hip).  Not installed; the public interface is
-// include/gcq.h.
+// gcq_internal.h -- declarations shared by the kernel files and the C ABI
+// (gcq_api.hip).  Not installed; the public interface is include/gcq.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include "gcq.h"
 
 namespace gcq {
 
@@ -31,27 +32,29 @@ struct Gc2Desc {
 
 // Worker pointers of the reduce, passed by value in the kernel arguments.
 struct DqWorkers {
-    const uint32_t *w[64];
+    const uint32_t *w[GCQ_MAX_WORKERS];
 };
 
-// Launch knobs (gcq_set_tuning in include/gcq.h); initial values from the
-// environment.  They change the launch shape only, never a result.
-struct Tuning {
-    int gc2_layout;        // 0: quad-assembled coalesced words, 1: per-lane runs
-    int nt;                // non-temporal hints on streamed data
-    int blocks_per_cu;     // 2-bit quantizer workgroups per CU (0: one tile each)
-    int dq_blocks_per_cu;  // reduce workgroups per CU (0: one word per thread)
-};
-Tuning tuning();
-void set_tuning(const Tuning &t);
+// Launch knobs (gcq_get_tuning / gcq_set_tuning).  They change the launch
+// shape only, never a result.
+gcq_tuning tuning();
+void set_tuning(const gcq_tuning &t);
+bool tuning_valid(const gcq_tuning &t);
 
 // Number of compute units of the current device (cached per device).
 int device_cus();
 
-// ---- launchers (return a hipError_t of the launch) --------------------
+// Grid size for `work_blocks` workgroups of work: all of them when
+// blocks_per_cu == 0, else at most blocks_per_cu per compute unit (the
+// kernel then strides); clamped to [1, 2^31 - 1].
+uint32_t grid_for(uint64_t work_blocks, int blocks_per_cu);
+
+// ---- launchers (return the hipError_t of the launch) -------------------
 hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream);
+// tiles_per_bucket > 0 when every bucket spans exactly that many tiles
+// (the kernel then finds its bucket by a division instead of a search).
 hipError_t launch_gc2_table(const Gc2Desc *dev_table, uint32_t nbuckets, uint64_t total_tiles,
-                            hipStream_t stream);
+                            uint32_t tiles_per_bucket, hipStream_t stream);
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t,
                                  float *acc, hipStream_t stream);
 hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t s, uint64_t seed,

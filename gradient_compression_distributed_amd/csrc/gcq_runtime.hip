@@ -1,0 +1,106 @@
+// gcq_runtime.hip -- host-side runtime state shared by the launchers:
+// launch knobs (defaults measured on MI355X, overridable from the
+// environment) and the per-device compute-unit count.
+#include <stdlib.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "gcq_internal.h"
+
+namespace gcq {
+
+namespace {
+
+std::mutex g_mu;
+bool g_init = false;
+gcq_tuning g_tuning;
+
+int env_int(const char *name, int dflt)
+{
+    const char *v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+int env_flag(const char *name, int dflt) { return env_int(name, dflt) ? 1 : 0; }
+
+int env_count(const char *name, int dflt)
+{
+    return std::max(0, std::min(1024, env_int(name, dflt)));
+}
+
+void init_locked()
+{
+    if (g_init)
+        return;
+    // Defaults: the fastest settings measured on MI355X at 2^30 elements.
+    g_tuning.gc2_layout = env_flag("GCQ_GC2_LAYOUT", 0);
+    g_tuning.gc2_nt = env_flag("GCQ_GC2_NT", 1);
+    g_tuning.gc2_blocks_per_cu = env_count("GCQ_GC2_BLOCKS_PER_CU", 0);
+    g_tuning.dq_nt_loads = env_flag("GCQ_DQ_NT_LOADS", 1);
+    g_tuning.dq_nt_stores = env_flag("GCQ_DQ_NT_STORES", 1);
+    g_tuning.dq_lds_stores = env_flag("GCQ_DQ_LDS_STORES", 1);
+    g_tuning.dq_blocks_per_cu = env_count("GCQ_DQ_BLOCKS_PER_CU", 0);
+    g_tuning.qsgd_nt = env_flag("GCQ_QSGD_NT", 1);
+    g_init = true;
+}
+
+bool flag_ok(int v) { return v == 0 || v == 1; }
+bool count_ok(int v) { return v >= 0 && v <= 1024; }
+
+}  // namespace
+
+gcq_tuning tuning()
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    init_locked();
+    return g_tuning;
+}
+
+bool tuning_valid(const gcq_tuning &t)
+{
+    return flag_ok(t.gc2_layout) && flag_ok(t.gc2_nt) && count_ok(t.gc2_blocks_per_cu) &&
+           flag_ok(t.dq_nt_loads) && flag_ok(t.dq_nt_stores) && flag_ok(t.dq_lds_stores) &&
+           count_ok(t.dq_blocks_per_cu) && flag_ok(t.qsgd_nt);
+}
+
+void set_tuning(const gcq_tuning &t)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    init_locked();
+    g_tuning = t;
+}
+
+int device_cus()
+{
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+uint32_t grid_for(uint64_t work_blocks, int blocks_per_cu)
+{
+    uint64_t g = work_blocks;
+    if (blocks_per_cu > 0) {
+        const uint64_t cap = (uint64_t)device_cus() * (uint64_t)blocks_per_cu;
+        g = g < cap ? g : cap;
+    }
+    if (g < 1)
+        g = 1;
+    if (g > 0x7FFFFFFFu)
+        g = 0x7FFFFFFFu;
+    return (uint32_t)g;
+}
+
+}  // namespace gcq

@@ -214,26 +214,46 @@ const char *gcq_status_string(int status);
 /* ------------------------------------------------------------------ */
 
 /*
- * gcq_set_tuning -- choose how the kernels map work to the GPU.  Every
- * setting produces bit-identical outputs.
- *   gc2_layout        0: lanes load 16-byte pieces side by side and each
- *                        quad of lanes assembles four packed words (default)
- *                     1: each lane owns a 64-byte run of 16 elements
- *   nt                1: non-temporal hints on streamed loads and stores
- *                        (default); 0: ordinary cached accesses
- *   blocks_per_cu     workgroups per compute unit of the 2-bit quantizer
- *                     (grid-stride); 0: one 4096-element tile per workgroup
- *                     (default)
- *   dq_blocks_per_cu  the same for gc2_dequant_reduce (0: one packed word
- *                     per thread, default)
- * A negative argument leaves that knob unchanged.  The initial values come
- * from the environment variables GCQ_GC2_LAYOUT, GCQ_NT, GCQ_BLOCKS_PER_CU
- * and GCQ_DQ_BLOCKS_PER_CU.  Takes effect for calls made after it returns;
- * it must not run concurrently with another call of this library.
- * Returns GCQ_OK, or GCQ_ERR_PARAM if a value is out of range (layout > 1,
- * nt > 1, a block count > 1024).
+ * How the kernels map work onto the GPU.  Every setting produces
+ * bit-identical outputs; only the time differs.
  */
-int gcq_set_tuning(int gc2_layout, int nt, int blocks_per_cu, int dq_blocks_per_cu);
+typedef struct gcq_tuning {
+    int gc2_layout;        /* 2-bit quantizer lane layout. 0: lanes load
+                              16-byte pieces side by side and each quad of
+                              lanes assembles four packed words (default);
+                              1: each lane owns a 64-byte run of 16 elements */
+    int gc2_nt;            /* 1: non-temporal hints on the quantizer's loads and
+                              stores (default 1) */
+    int gc2_blocks_per_cu; /* 0: one 4096-element tile per workgroup (default);
+                              k > 0: k workgroups per compute unit, grid-stride */
+    int dq_nt_loads;       /* 1: non-temporal loads of the packed words in
+                              gc2_dequant_reduce */
+    int dq_nt_stores;      /* 1: non-temporal stores of the sums */
+    int dq_lds_stores;     /* 1: stage each wavefront's sums through LDS so
+                              every store instruction writes 1 KiB of
+                              consecutive memory; 0: each lane stores its 16
+                              consecutive sums directly */
+    int dq_blocks_per_cu;  /* 0: one packed word position per thread (default);
+                              k > 0: k workgroups per compute unit, grid-stride */
+    int qsgd_nt;           /* 1: non-temporal hints in the QSGD kernels */
+} gcq_tuning;
+
+/*
+ * gcq_get_tuning -- copy the current knobs into *out (host struct).  The
+ * initial values are the library defaults, overridden by the environment
+ * variables GCQ_GC2_LAYOUT, GCQ_GC2_NT, GCQ_GC2_BLOCKS_PER_CU,
+ * GCQ_DQ_NT_LOADS, GCQ_DQ_NT_STORES, GCQ_DQ_LDS_STORES,
+ * GCQ_DQ_BLOCKS_PER_CU and GCQ_QSGD_NT when set.
+ * Errors: GCQ_ERR_NULL.
+ *
+ * gcq_set_tuning -- replace the knobs with *t (host struct).  Takes effect
+ * for calls made after it returns; it must not run concurrently with
+ * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
+ * flag not 0/1, a layout not 0/1, a block count outside 0..1024); on error
+ * nothing changes.
+ */
+int gcq_get_tuning(gcq_tuning *out);
+int gcq_set_tuning(const gcq_tuning *t);
 
 #ifdef __cplusplus
 }

@@ -149,3 +149,24 @@ def test_binding_refuses_host_tensors():
     g = torch.zeros(16)
     with pytest.raises(ValueError):
         gcq.gc2_quantize(g, torch.zeros(16), 0.5)
+
+
+def test_tuning_roundtrip_and_validation(lib):
+    t = gcq.Tuning()
+    assert lib.gcq_get_tuning(ctypes.byref(t)) == OK
+    saved = t.as_dict()
+    assert saved["gc2_layout"] in (0, 1) and saved["gc2_blocks_per_cu"] >= 0
+    assert lib.gcq_get_tuning(None) == E_NULL
+    assert lib.gcq_set_tuning(None) == E_NULL
+    for field, bad in [("gc2_layout", 2), ("gc2_nt", -1), ("dq_lds_stores", 5),
+                       ("gc2_blocks_per_cu", 1025), ("dq_blocks_per_cu", -3), ("qsgd_nt", 7)]:
+        b = gcq.Tuning(**saved)
+        setattr(b, field, bad)
+        assert lib.gcq_set_tuning(ctypes.byref(b)) == E_PARAM, field
+    t2 = gcq.Tuning()
+    lib.gcq_get_tuning(ctypes.byref(t2))
+    assert t2.as_dict() == saved                      # a rejected set changes nothing
+    old = gcq.set_tuning(gc2_blocks_per_cu=7, dq_nt_stores=1)
+    assert gcq.get_tuning()["gc2_blocks_per_cu"] == 7
+    gcq.set_tuning(**old)
+    assert gcq.get_tuning() == saved

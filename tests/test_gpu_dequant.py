@@ -43,15 +43,20 @@ def test_config3_w16(gpu):
     assert np.array_equal(bits(host(acc_d)), bits(acc_h))
 
 
-@pytest.mark.parametrize("dq_bpc", [0, 4])
-def test_workers_sizes_thresholds(gpu, dq_bpc):
+DQ_VARIANTS = [dict(dq_nt_loads=l, dq_nt_stores=s, dq_lds_stores=d, dq_blocks_per_cu=b)
+               for (l, s, d, b) in [(1, 0, 1, 0), (1, 0, 0, 0), (0, 1, 1, 4), (0, 0, 0, 2),
+                                    (1, 1, 0, 0), (0, 0, 1, 1), (1, 1, 1, 8), (0, 1, 0, 0)]]
+
+
+@pytest.mark.parametrize("var", range(len(DQ_VARIANTS)))
+def test_workers_sizes_thresholds(gpu, var):
     import torch
 
-    gpu.set_tuning(dq_blocks_per_cu=dq_bpc)
+    old = gpu.set_tuning(**DQ_VARIANTS[var])
     try:
-        rs = np.random.default_rng(21 + dq_bpc)
+        rs = np.random.default_rng(21 + var)
         for W in (1, 2, 3, 7, 15, 16, 17, 31, 33, 64):
-            for n in (1, 15, 16, 17, 63, 4095, 4097, 100_003):
+            for n in (1, 15, 16, 17, 63, 4095, 4096, 4097, 8192, 100_003):
                 # t = 1e-37 exercises the path for thresholds below 2^-120
                 t = float(rs.choice([0.01, 1e-3, 0.5, 0.1, 7.7, 1e-37]))
                 say("dequant W", W, "n", n, "t", t)
@@ -67,7 +72,7 @@ def test_workers_sizes_thresholds(gpu, dq_bpc):
                 assert np.array_equal(bits(out[:n]), bits(acc_h)), (W, n, t)
                 assert np.all(out[n:] == np.float32(1234.5))
     finally:
-        gpu.set_tuning(dq_blocks_per_cu=0)
+        gpu.set_tuning(**old)
 
 
 def test_aliased_workers(gpu):

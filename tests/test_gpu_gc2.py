@@ -36,14 +36,17 @@ def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-VARIANTS = [dict(gc2_layout=0, nt=1, blocks_per_cu=0), dict(gc2_layout=1, nt=1, blocks_per_cu=0),
-            dict(gc2_layout=0, nt=0, blocks_per_cu=8), dict(gc2_layout=1, nt=0, blocks_per_cu=2)]
+VARIANTS = [dict(gc2_layout=0, gc2_nt=1, gc2_blocks_per_cu=0),
+            dict(gc2_layout=1, gc2_nt=1, gc2_blocks_per_cu=0),
+            dict(gc2_layout=0, gc2_nt=0, gc2_blocks_per_cu=8),
+            dict(gc2_layout=1, gc2_nt=0, gc2_blocks_per_cu=2)]
 
 
 @pytest.fixture
 def default_tuning(gpu):
+    old = gpu.get_tuning()
     yield gpu
-    gpu.set_tuning(gc2_layout=0, nt=1, blocks_per_cu=0)
+    gpu.set_tuning(**old)
 
 
 def test_config1_three_steps(gpu):
@@ -227,6 +230,75 @@ def test_buckets_fused_equals_per_bucket_and_oracle(default_tuning, var):
             n, nw = a.size, oracle.packed_words(a.size)
             assert np.array_equal(host(obuf[ooff[i]:ooff[i] + nw]), w_h), (step, i)
             assert np.array_equal(bits(host(rbuf[roff[i]:roff[i] + n])), bits(rs_[i])), (step, i)
+
+
+@pytest.mark.parametrize("var", [0, 2])
+def test_buckets_equal_tile_counts(default_tuning, var):
+    # every bucket spans the same number of 4096-element tiles (the kernel
+    # then maps a tile to its bucket by a division), with different n inside
+    import torch
+
+    gpu = default_tuning
+    gpu.set_tuning(**VARIANTS[var])
+    say("gc2 equal-tile buckets variant", VARIANTS[var])
+    rs = np.random.default_rng(8 + var)
+    sizes = [8192, 4097, 6000, 8192, 5555, 8191, 4100] * 3
+    t = 0.01
+    gs = [(rs.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    r_h = [np.zeros(n, np.float32) for n in sizes]
+    g_d = [dev(a) for a in gs]
+    r_d = [torch.zeros(n, device="cuda") for n in sizes]
+    o_d = [torch.full((oracle.packed_words(n) + 8,), 0x5A5A5A5A, dtype=torch.int32,
+                      device="cuda") for n in sizes]
+    bl = gpu.BucketList([(g_d[i], r_d[i], o_d[i][:oracle.packed_words(n)], t)
+                         for i, n in enumerate(sizes)])
+    for step in range(2):
+        gpu.gc2_quantize_buckets(bl)
+        torch.cuda.synchronize()
+        for i, n in enumerate(sizes):
+            w_h = oracle.gc2_quantize(gs[i], r_h[i], t)
+            out = host(o_d[i])
+            assert np.array_equal(out[:w_h.size], w_h), (step, i)
+            assert np.all(out[w_h.size:] == 0x5A5A5A5A)
+            assert np.array_equal(bits(host(r_d[i])), bits(r_h[i])), (step, i)
+
+
+def test_bucket_table_reuse_across_streams(gpu):
+    # identical descriptors reuse the device table; a call on a second
+    # stream must still run after the first one (it reads the residual the
+    # first one wrote), and a different bucket list in between must not
+    # disturb either
+    import torch
+
+    say("gc2 table reuse across streams")
+    rs = np.random.default_rng(31)
+    sizes = [30_000, 4096, 12_289, 777]
+    t = 0.05
+    gs = [(rs.standard_normal(n) * 0.04).astype(np.float32) for n in sizes]
+    g_d = [dev(a) for a in gs]
+    r_d = [torch.zeros(n, device="cuda") for n in sizes]
+    o_d = [torch.empty(oracle.packed_words(n), dtype=torch.int32, device="cuda") for n in sizes]
+    A = gpu.BucketList([(g_d[i], r_d[i], o_d[i], t) for i in range(len(sizes))])
+    g2 = dev((rs.standard_normal(5000) * 0.04).astype(np.float32))
+    r2 = torch.zeros(5000, device="cuda")
+    o2 = torch.empty(oracle.packed_words(5000), dtype=torch.int32, device="cuda")
+    B = gpu.BucketList([(g2, r2, o2, t)])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    r_h = [np.zeros(n, np.float32) for n in sizes]
+    for step, stream in enumerate([s1, s2, s2, s1]):
+        with torch.cuda.stream(stream):
+            if step == 2:
+                gpu.gc2_quantize_buckets(B)
+            gpu.gc2_quantize_buckets(A)
+        want = [oracle.gc2_quantize(gs[i], r_h[i], t) for i in range(len(sizes))]
+        if step == 1:
+            s2.synchronize()        # only s2: the s1 launch must already be ordered before it
+        else:
+            torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            assert np.array_equal(host(o_d[i]), want[i]), (step, i)
+            assert np.array_equal(bits(host(r_d[i])), bits(r_h[i])), (step, i)
 
 
 def _code_properties(w32, r_new, v, t):
