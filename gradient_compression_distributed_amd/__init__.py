@@ -39,7 +39,8 @@ class Tuning(ctypes.Structure):
     """Mirror of ``gcq_tuning`` (launch knobs; results never depend on them)."""
     _fields_ = [(f, ctypes.c_int) for f in (
         "gc2_layout", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
-        "dq_lds_stores", "dq_blocks_per_cu", "qsgd_nt")]
+        "dq_lds_stores", "dq_blocks_per_cu", "dq_fp4_decode", "qsgd_nt", "qsgd_rcp",
+        "qsgd_dequant_nt")]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

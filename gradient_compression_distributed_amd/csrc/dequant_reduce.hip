@@ -28,18 +28,50 @@ __device__ __forceinline__ uint32_t signed_pairs(uint32_t w)
     return (hi & ~lo_at_hi) | (hi >> 1);
 }
 
-// Add one worker's word (16 codes) into the 16 running sums.  Element k's
-// value f_k in {-1, 0, +1} is moved to the top two bits of a byte
-// (m_r = (pairs << 2r) & 0xC0C0C0C0 holds elements r, 4+r, 8+r, 12+r in
-// bytes 3, 2, 1, 0), so one signed-byte conversion (an SDWA v_cvt) yields
-// 64 f_k exactly.  With tq = t/64 (exact: t >= 2^-120), fma(tq, 64 f_k, a)
-// rounds t f_k + a once: the same result as a + (+t | -t | 0) in float32.
-// Scaled = false does the same with f_k itself and tq = t (tiny t).
-template <bool Scaled>
+// Add one worker's word (16 codes) into the 16 running sums, in one of
+// three decodes (Mode), each exact:
+//
+// kDecodeFp4: the signed pairs are masked to the top two bits of each
+//   nibble (me: pairs 0, 2, .., 14; mo: pairs 1, 3, .., 15, in nibbles 7..0),
+//   which makes each nibble the FP4 (E2M1) code of +2.0 (0100), -2.0 (1100)
+//   or 0 (0000).  One v_cvt_scalef32_pk_f32_fp4 (scale 1) turns a byte, i.e.
+//   two elements, into two exact floats (low nibble -> .x).  With
+//   tq = t/2 (exact for t >= 2^-120), fma(tq, 2 f, a) rounds t f + a once:
+//   the same result as a + (+t | -t | 0) in float32.
+// kDecodeSdwa: the pairs are masked to the top of each byte (m_r =
+//   (pairs << 2r) & 0xC0C0C0C0 holds elements r, 4+r, 8+r, 12+r in bytes
+//   3..0) and one signed-byte conversion (SDWA v_cvt) gives 64 f exactly;
+//   tq = t/64.
+// kDecodePlain: f from a sign-extending shift, tq = t (any t, including
+//   t < 2^-120, where t/2 or t/64 would not be exact).
+enum { kDecodeFp4 = 0, kDecodeSdwa = 1, kDecodePlain = 2 };
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Byte B of the masked words: nibble 2B holds pair 14-4B (me) / 15-4B (mo),
+// nibble 2B+1 pair 12-4B / 13-4B.
+template <int B>
+__device__ __forceinline__ void fp4_byte(float (&a)[16], uint32_t me, uint32_t mo, float tq)
+{
+    const v2f e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(me, 1.0f, B);
+    const v2f o = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(mo, 1.0f, B);
+    a[14 - 4 * B] = __builtin_fmaf(tq, e.x, a[14 - 4 * B]);
+    a[12 - 4 * B] = __builtin_fmaf(tq, e.y, a[12 - 4 * B]);
+    a[15 - 4 * B] = __builtin_fmaf(tq, o.x, a[15 - 4 * B]);
+    a[13 - 4 * B] = __builtin_fmaf(tq, o.y, a[13 - 4 * B]);
+}
+
+template <int Mode>
 __device__ __forceinline__ void accumulate(float (&a)[16], uint32_t w, float tq)
 {
     const uint32_t pairs = signed_pairs(w);
-    if constexpr (Scaled) {
+    if constexpr (Mode == kDecodeFp4) {
+        const uint32_t me = pairs & 0xCCCCCCCCu;
+        const uint32_t mo = (pairs << 2) & 0xCCCCCCCCu;
+        fp4_byte<0>(a, me, mo, tq);
+        fp4_byte<1>(a, me, mo, tq);
+        fp4_byte<2>(a, me, mo, tq);
+        fp4_byte<3>(a, me, mo, tq);
+    } else if constexpr (Mode == kDecodeSdwa) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t m = (pairs << (2 * r)) & 0xC0C0C0C0u;
@@ -71,7 +103,7 @@ constexpr int kLdsRow = 16;     // floats per staged row (one packed word's sums
 // LDS and reads them back transposed, so lane L stores elements
 // 256q + 4L .. +3 (q = 0..3): every store instruction writes 1 KiB of
 // consecutive memory instead of 64 scattered 16-byte pieces.
-template <bool Scaled, bool NTL, bool NTS, bool Lds>
+template <int Mode, bool NTL, bool NTS, bool Lds>
 __global__ __launch_bounds__(kBlockThreads) void dq_reduce_kernel(DqWorkers ws, uint32_t W,
                                                                   uint32_t nwords, uint64_t n,
                                                                   float tq, float *__restrict__ acc)
@@ -89,19 +121,24 @@ __global__ __launch_bounds__(kBlockThreads) void dq_reduce_kernel(DqWorkers ws, 
             a[k] = 0.0f;
         if (valid) {
             const uint32_t boff = wi * 4u;
-            for (uint32_t w0 = 0; w0 < W; w0 += kChunk) {
+            uint32_t w0 = 0;
+            // whole groups of kChunk workers: all loads issued, then decoded
+            for (; w0 + kChunk <= W; w0 += kChunk) {
                 uint32_t wd[kChunk];
 #pragma unroll
                 for (int j = 0; j < kChunk; ++j)
-                    wd[j] = (w0 + j < W)
-                                ? ld<NTL>((const GCQ_GLOBAL uint32_t *)(
-                                      (const GCQ_GLOBAL char *)ws.w[w0 + j] + boff))
-                                : 0u;
+                    wd[j] = ld<NTL>((const GCQ_GLOBAL uint32_t *)(
+                        (const GCQ_GLOBAL char *)ws.w[w0 + j] + boff));
 #pragma unroll
                 for (int j = 0; j < kChunk; ++j)
-                    if (w0 + j < W)
-                        accumulate<Scaled>(a, wd[j], tq);
+                    accumulate<Mode>(a, wd[j], tq);
             }
+            // the rest, one worker at a time (still in worker order)
+            for (; w0 < W; ++w0)
+                accumulate<Mode>(a,
+                                 ld<NTL>((const GCQ_GLOBAL uint32_t *)(
+                                     (const GCQ_GLOBAL char *)ws.w[w0] + boff)),
+                                 tq);
         }
         const uint64_t e = (uint64_t)wi * 16u;
         if (Lds && ((uint64_t)base + kBlockThreads) * 16u <= n) {
@@ -147,28 +184,28 @@ __global__ __launch_bounds__(kBlockThreads) void dq_reduce_kernel(DqWorkers ws, 
     }
 }
 
-template <bool Scaled, bool NTL, bool NTS, bool Lds>
+template <int Mode, bool NTL, bool NTS, bool Lds>
 void launch_one(uint32_t grid, hipStream_t stream, const DqWorkers &ws, uint32_t W,
                 uint32_t nwords, uint64_t n, float tq, float *acc)
 {
-    dq_reduce_kernel<Scaled, NTL, NTS, Lds>
+    dq_reduce_kernel<Mode, NTL, NTS, Lds>
         <<<grid, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
 }
 
-template <bool Scaled>
+template <int Mode>
 void dispatch(const gcq_tuning &tu, uint32_t grid, hipStream_t stream, const DqWorkers &ws,
               uint32_t W, uint32_t nwords, uint64_t n, float tq, float *acc)
 {
     const int key = tu.dq_nt_loads * 4 + tu.dq_nt_stores * 2 + tu.dq_lds_stores;
     switch (key) {
-    case 0: launch_one<Scaled, false, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 1: launch_one<Scaled, false, false, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 2: launch_one<Scaled, false, true, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 3: launch_one<Scaled, false, true, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 4: launch_one<Scaled, true, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 5: launch_one<Scaled, true, false, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 6: launch_one<Scaled, true, true, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    default: launch_one<Scaled, true, true, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 0: launch_one<Mode, false, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 1: launch_one<Mode, false, false, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 2: launch_one<Mode, false, true, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 3: launch_one<Mode, false, true, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 4: launch_one<Mode, true, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 5: launch_one<Mode, true, false, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 6: launch_one<Mode, true, true, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    default: launch_one<Mode, true, true, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
     }
 }
 
@@ -184,9 +221,10 @@ hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, flo
     if (!nwords)
         return hipSuccess;
     const gcq_tuning tu = tuning();
-    // t/64 is exact (a power-of-two scaling that stays normal) for t >= 2^-120.
-    const bool scaled = t >= 0x1p-120f;
-    const float tq = scaled ? t * 0x1p-6f : t;
+    // t/2 and t/64 are exact (power-of-two scalings that stay normal) for
+    // t >= 2^-120; smaller thresholds use the plain decode.
+    const int mode = t < 0x1p-120f ? kDecodePlain : (tu.dq_fp4_decode ? kDecodeFp4 : kDecodeSdwa);
+    const float tq = mode == kDecodeFp4 ? t * 0.5f : (mode == kDecodeSdwa ? t * 0x1p-6f : t);
     for (uint64_t w0 = 0; w0 < nwords; w0 += kMaxWordsPerLaunch) {
         const uint64_t cw = nwords - w0 < kMaxWordsPerLaunch ? nwords - w0 : kMaxWordsPerLaunch;
         const uint64_t cn = (n - w0 * 16) < cw * 16 ? (n - w0 * 16) : cw * 16;
@@ -195,10 +233,12 @@ hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, flo
             ws.w[k] = w.w[k] + w0;
         const uint32_t grid =
             grid_for((cw + kBlockThreads - 1) / kBlockThreads, tu.dq_blocks_per_cu);
-        if (scaled)
-            dispatch<true>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
+        if (mode == kDecodeFp4)
+            dispatch<kDecodeFp4>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
+        else if (mode == kDecodeSdwa)
+            dispatch<kDecodeSdwa>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
         else
-            dispatch<false>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
+            dispatch<kDecodePlain>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -34,9 +34,13 @@ __device__ __forceinline__ float gc2_residual(float v, uint32_t code, float t)
     return v - sent;
 }
 
+// Non-temporal hints per operand (a bit mask): g loads, r loads, r stores,
+// packed-word stores.
+constexpr int kNtG = 1, kNtR = 2, kNtRStore = 4, kNtOut = 8, kNtAll = 15;
+
 // Four elements -> their residuals (stored) and one byte of codes, first
 // element in the top bit pair.
-template <bool NT, typename RP>
+template <int NT, typename RP>
 __device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
 {
     const v4f v = g + r;
@@ -47,7 +51,7 @@ __device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
     rn.y = gc2_residual(v.y, c1, t);
     rn.z = gc2_residual(v.z, c2, t);
     rn.w = gc2_residual(v.w, c3, t);
-    st<NT>(rout, rn);
+    st<(NT & kNtRStore) != 0>(rout, rn);
     return (c0 << 6) | (c1 << 4) | (c2 << 2) | c3;
 }
 
@@ -58,7 +62,7 @@ __device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
 // the four bytes of four words; one DPP broadcast per source lane lets lane
 // 4m + j assemble word 16j + m, so the wave stores its 64 words as one
 // 256-byte block.
-template <bool NT>
+template <int NT>
 __device__ __forceinline__ void gc2_tile_coalesced(const GCQ_GLOBAL float *__restrict__ g,
                                                    GCQ_GLOBAL float *__restrict__ r,
                                                    GCQ_GLOBAL uint32_t *__restrict__ out, float t,
@@ -69,8 +73,8 @@ __device__ __forceinline__ void gc2_tile_coalesced(const GCQ_GLOBAL float *__res
     v4f gv[4], rv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        gv[k] = ld<NT>(g4 + k * kWave + lane);
-        rv[k] = ld<NT>(r4 + k * kWave + lane);
+        gv[k] = ld<(NT & kNtG) != 0>(g4 + k * kWave + lane);
+        rv[k] = ld<(NT & kNtR) != 0>(r4 + k * kWave + lane);
     }
     uint32_t bytes = 0;
 #pragma unroll
@@ -81,13 +85,13 @@ __device__ __forceinline__ void gc2_tile_coalesced(const GCQ_GLOBAL float *__res
     const uint32_t j = lane & 3u, sh = 8u * j;
     const uint32_t word = (((x0 >> sh) & 0xFFu) << 24) | (((x1 >> sh) & 0xFFu) << 16) |
                           (((x2 >> sh) & 0xFFu) << 8) | ((x3 >> sh) & 0xFFu);
-    st<NT>(out + 16u * j + (lane >> 2), word);
+    st<(NT & kNtOut) != 0>(out + 16u * j + (lane >> 2), word);
 }
 
 // Full wave tile, layout 1: lane L owns elements 16L .. 16L+15 (a 64-byte
 // run, four dwordx4 loads 64 bytes apart across lanes) and packs its own
 // word with no cross-lane traffic.
-template <bool NT>
+template <int NT>
 __device__ __forceinline__ void gc2_tile_runs(const GCQ_GLOBAL float *__restrict__ g,
                                               GCQ_GLOBAL float *__restrict__ r,
                                               GCQ_GLOBAL uint32_t *__restrict__ out, float t,
@@ -98,14 +102,14 @@ __device__ __forceinline__ void gc2_tile_runs(const GCQ_GLOBAL float *__restrict
     v4f gv[4], rv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        gv[k] = ld<NT>(g4 + k);
-        rv[k] = ld<NT>(r4 + k);
+        gv[k] = ld<(NT & kNtG) != 0>(g4 + k);
+        rv[k] = ld<(NT & kNtR) != 0>(r4 + k);
     }
     uint32_t word = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         word |= gc2_quad<NT>(gv[k], rv[k], t, r4 + k) << (24 - 8 * k);
-    st<NT>(out + lane, word);
+    st<(NT & kNtOut) != 0>(out + lane, word);
 }
 
 // Wave tile that runs past the end of its bucket: lane L packs word
@@ -159,7 +163,7 @@ __device__ __forceinline__ uint32_t gc2_find_bucket(const Gc2Desc *__restrict__ 
 // tile (the default) it runs once.  A block tile is 16 KiB-aligned within
 // its bucket, so no cache line is shared between workgroups, and thus
 // between the XCDs' L2 caches.
-template <int Layout, bool NT, bool Table>
+template <int Layout, int NT, bool Table>
 __global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
     Gc2Desc one, const Gc2Desc *__restrict__ table, uint32_t nbuckets, uint64_t total_tiles,
     uint32_t tiles_per_bucket)
@@ -208,16 +212,31 @@ hipError_t launch(const Gc2Desc &one, const Gc2Desc *table, uint32_t nb, uint64_
     const dim3 block(kBlockThreads);
 #define GCQ_GC2(L, NT) \
     gc2_quantize_kernel<L, NT, Table><<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb)
-    if (tu.gc2_layout == 0) {
+    if (tu.gc2_layout == 1) {
+        // layout 1 only in the all / none forms
         if (tu.gc2_nt)
-            GCQ_GC2(0, true);
+            GCQ_GC2(1, kNtAll);
         else
-            GCQ_GC2(0, false);
+            GCQ_GC2(1, 0);
     } else {
-        if (tu.gc2_nt)
-            GCQ_GC2(1, true);
-        else
-            GCQ_GC2(1, false);
+        switch (tu.gc2_nt) {
+        case 0: GCQ_GC2(0, 0); break;
+        case 1: GCQ_GC2(0, 1); break;
+        case 2: GCQ_GC2(0, 2); break;
+        case 3: GCQ_GC2(0, 3); break;
+        case 4: GCQ_GC2(0, 4); break;
+        case 5: GCQ_GC2(0, 5); break;
+        case 6: GCQ_GC2(0, 6); break;
+        case 7: GCQ_GC2(0, 7); break;
+        case 8: GCQ_GC2(0, 8); break;
+        case 9: GCQ_GC2(0, 9); break;
+        case 10: GCQ_GC2(0, 10); break;
+        case 11: GCQ_GC2(0, 11); break;
+        case 12: GCQ_GC2(0, 12); break;
+        case 13: GCQ_GC2(0, 13); break;
+        case 14: GCQ_GC2(0, 14); break;
+        default: GCQ_GC2(0, 15); break;
+        }
     }
 #undef GCQ_GC2
     return hipGetLastError();

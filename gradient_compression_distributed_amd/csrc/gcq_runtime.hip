@@ -35,13 +35,16 @@ void init_locked()
         return;
     // Defaults: the fastest settings measured on MI355X at 2^30 elements.
     g_tuning.gc2_layout = env_flag("GCQ_GC2_LAYOUT", 0);
-    g_tuning.gc2_nt = env_flag("GCQ_GC2_NT", 1);
+    g_tuning.gc2_nt = std::max(0, std::min(15, env_int("GCQ_GC2_NT", 7)));
     g_tuning.gc2_blocks_per_cu = env_count("GCQ_GC2_BLOCKS_PER_CU", 0);
     g_tuning.dq_nt_loads = env_flag("GCQ_DQ_NT_LOADS", 1);
     g_tuning.dq_nt_stores = env_flag("GCQ_DQ_NT_STORES", 1);
     g_tuning.dq_lds_stores = env_flag("GCQ_DQ_LDS_STORES", 1);
     g_tuning.dq_blocks_per_cu = env_count("GCQ_DQ_BLOCKS_PER_CU", 0);
-    g_tuning.qsgd_nt = env_flag("GCQ_QSGD_NT", 1);
+    g_tuning.dq_fp4_decode = env_flag("GCQ_DQ_FP4_DECODE", 1);
+    g_tuning.qsgd_nt = env_flag("GCQ_QSGD_NT", 0);
+    g_tuning.qsgd_rcp = env_flag("GCQ_QSGD_RCP", 1);
+    g_tuning.qsgd_dequant_nt = env_flag("GCQ_QSGD_DEQUANT_NT", 1);
     g_init = true;
 }
 
@@ -59,9 +62,10 @@ gcq_tuning tuning()
 
 bool tuning_valid(const gcq_tuning &t)
 {
-    return flag_ok(t.gc2_layout) && flag_ok(t.gc2_nt) && count_ok(t.gc2_blocks_per_cu) &&
+    return flag_ok(t.gc2_layout) && t.gc2_nt >= 0 && t.gc2_nt <= 15 && count_ok(t.gc2_blocks_per_cu) &&
            flag_ok(t.dq_nt_loads) && flag_ok(t.dq_nt_stores) && flag_ok(t.dq_lds_stores) &&
-           count_ok(t.dq_blocks_per_cu) && flag_ok(t.qsgd_nt);
+           count_ok(t.dq_blocks_per_cu) && flag_ok(t.dq_fp4_decode) && flag_ok(t.qsgd_nt) &&
+           flag_ok(t.qsgd_rcp) && flag_ok(t.qsgd_dequant_nt);
 }
 
 void set_tuning(const gcq_tuning &t)

@@ -23,7 +23,8 @@ using dev::v4f;
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64-bit products; the high halves are xored with the other counter
 // words and the round key, the words permuted; the key advances by the
-// Weyl increments between rounds.
+// Weyl increments between rounds.  Each product is one v_mad_u64_u32 and
+// each three-way xor one v_bitop3_b32 (truth table 0x96) on gfx950.
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1)
 {
 #pragma unroll
@@ -32,13 +33,14 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t a = c[0], b = c[2];
-        const uint32_t lo0 = 0xD2511F53u * a, hi0 = __umulhi(0xD2511F53u, a);
-        const uint32_t lo1 = 0xCD9E8D57u * b, hi1 = __umulhi(0xCD9E8D57u, b);
-        c[0] = hi1 ^ c[1] ^ k0;
-        c[1] = lo1;
-        c[2] = hi0 ^ c[3] ^ k1;
-        c[3] = lo0;
+        const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
+        c[0] = n0;
+        c[1] = (uint32_t)p1;
+        c[2] = n2;
+        c[3] = (uint32_t)p0;
     }
 }
 
@@ -53,10 +55,11 @@ __device__ __forceinline__ void uniforms4(uint64_t q, uint32_t k0, uint32_t k1, 
         u[j] = (float)(c[j] >> 8) * 0x1p-24f;
 }
 
-// Level of one element (Knowl 1): a = |g|/norm, x = a s, l = floor(x),
-// level l+1 with probability x - l; zero norm -> 0; x >= s -> s; NaN -> 0.
-__device__ __forceinline__ uint32_t qsgd_level(float gabs, float norm, float sf, uint32_t s,
-                                               float u)
+// Level of one element (Knowl 1), exactly as defined: a = |g|/norm (one
+// correctly rounded division), x = a s, l = floor(x), level l+1 when
+// u < x - l; zero norm -> 0; x >= s -> s; NaN -> 0.
+__device__ __forceinline__ uint32_t qsgd_level_exact(float gabs, float norm, float sf, uint32_t s,
+                                                     float u)
 {
     const float a = gabs / norm;
     const float x = a * sf;
@@ -72,11 +75,40 @@ __device__ __forceinline__ uint32_t qsgd_level(float gabs, float norm, float sf,
     return level;
 }
 
-__device__ __forceinline__ uint32_t qsgd_nibble(float gv, float norm, float sf, uint32_t s,
-                                                float u)
+// The same level without a division per element.  For a bucket norm in
+// [2^-120, 2^120], x' = |g| * rs with rs = RN(RN(1/norm) * s) differs from
+// the exact x = RN(RN(|g|/norm) * s) by less than 40 * 2^-24 < 2^-18.6 (five
+// relative roundings of at most 2^-24 each on a value below 7.0001, since
+// |g| <= norm up to its own rounding; all intermediates are normal
+// whenever x' > 2^-18).  So when no integer and no u lies within
+// kGuard = 2^-18 of x', floor and the comparison with u come out the same
+// as for the exact x.  That also settles the clamp at s: x' <= s (1 + 2^-22)
+// < s + kGuard, so an x' near s is near an integer.  g == 0 is exact
+// (x' = x = 0).  `safe` is false for the lanes (a few per million) that
+// must take the exact path.
+constexpr float kGuard = 0x1p-18f;
+
+__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, float u, bool &safe)
 {
-    const uint32_t sign = gv < 0.0f ? 8u : 0u;
-    return sign | qsgd_level(fabsf(gv), norm, sf, s, u);
+    const float x = gabs * rs;               // <= 7.001: the conversion stays in range
+    const float l = floorf(x);
+    const float p = x - l;                   // exact
+    safe = gabs == 0.0f || (p > kGuard && p < 1.0f - kGuard && fabsf(u - p) > kGuard);
+    return (uint32_t)l + (u < p ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t sign_bit(float gv) { return gv < 0.0f ? 8u : 0u; }
+
+// A bucket takes the division-free level path when its norm is in this
+// range (false for 0, Inf and NaN norms, which take the exact path).
+__device__ __forceinline__ bool rcp_norm_ok(float norm)
+{
+    return norm >= 0x1p-120f && norm <= 0x1p120f;
+}
+
+__device__ __forceinline__ float uniform_f(float x)
+{
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
 
 __device__ __forceinline__ double wave_sum(double x)
@@ -91,11 +123,12 @@ __device__ __forceinline__ double wave_sum(double x)
 // registers: one wavefront per bucket, lane L holds elements 256c + 4L .. +3
 // (dwordx4 loads, 1 KiB per wave instruction).  The sum of squares is
 // accumulated in float64 (each square exact), reduced across the wave by
-// butterfly shuffles, square-rooted in float64 and rounded once to float32.
-// Nibble words: lane pairs (2m, 2m+1) hold the two halves of word 32c + m
-// of chunk c; one DPP neighbour swap per two chunks lets even lanes store
-// chunk c's words and odd lanes chunk c+1's.
-template <int C, bool NT>
+// butterfly shuffles, square-rooted in float64 and rounded once to float32;
+// the norm is then wave-uniform (a scalar register).  Nibble words: lane
+// pairs (2m, 2m+1) hold the two halves of word 32c + m of chunk c; one DPP
+// neighbour swap per two chunks lets even lanes store chunk c's words and
+// odd lanes chunk c+1's.
+template <int C, bool NT, bool Rcp>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
     const float *__restrict__ g, uint32_t s, uint32_t k0, uint32_t k1, float *__restrict__ norms,
     uint32_t *__restrict__ nib, uint64_t nb_full)
@@ -111,6 +144,12 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c)
             v[c] = ld<NT>(reinterpret_cast<const v4f *>(g + base + 256u * c) + lane);
+        // the draws do not depend on the norm: computing them first overlaps
+        // the Philox arithmetic with the latency of the wave reduction
+        float u[C][4];
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            uniforms4((base + 256u * c + 4u * lane) >> 2, k0, k1, u[c]);
         double ss = 0.0;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -120,18 +159,37 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
             ss = __builtin_fma((double)v[c].w, (double)v[c].w, ss);
         }
         ss = wave_sum(ss);
-        const float norm = (float)__builtin_sqrt(ss);
+        const float norm = uniform_f((float)__builtin_sqrt(ss));
         if (lane == 0)
             norms[b] = norm;
+        const bool fast = Rcp && rcp_norm_ok(norm);
+        const float rs = fast ? (1.0f / norm) * sf : 0.0f;
         uint32_t h[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            float u[4];
-            uniforms4((base + 256u * c + 4u * lane) >> 2, k0, k1, u);
-            h[c] = (qsgd_nibble(v[c].x, norm, sf, s, u[0]) << 12) |
-                   (qsgd_nibble(v[c].y, norm, sf, s, u[1]) << 8) |
-                   (qsgd_nibble(v[c].z, norm, sf, s, u[2]) << 4) |
-                   qsgd_nibble(v[c].w, norm, sf, s, u[3]);
+            const float gq[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+            uint32_t lv[4];
+            if (fast) {
+                bool ok[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, u[c][q], ok[q]);
+                if (!(ok[0] && ok[1] && ok[2] && ok[3])) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (!ok[q])
+                            lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, u[c][q]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, u[c][q]);
+            }
+            uint32_t hv = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                hv |= (sign_bit(gq[q]) | lv[q]) << (12 - 4 * q);
+            h[c] = hv;
         }
         uint32_t *out = nib + (base >> 3);
         const bool odd = (lane & 1u) != 0;
@@ -208,7 +266,8 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_levels_generic_kernel(
             for (uint32_t q = 0; q < 4; ++q) {
                 const uint64_t e = eb + q;
                 if (e < n) {
-                    const uint32_t nbl = qsgd_nibble(g[e], norms[e / d], sf, s, u[q]);
+                    const uint32_t nbl =
+                        sign_bit(g[e]) | qsgd_level_exact(fabsf(g[e]), norms[e / d], sf, s, u[q]);
                     word |= nbl << (28u - 4u * (4u * half + q));
                 }
             }
@@ -217,52 +276,67 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_levels_generic_kernel(
     }
 }
 
-// Decode (Knowl 3): out = +-((norm * level) / s).  One thread per group of 4
-// elements (a 16-byte store); lanes 2m and 2m+1 read the two halves of one
-// nibble word.  Pow2: d is a power of two >= 4, so the group shares one
-// bucket and the bucket index is a shift.
+// Decode (Knowl 3): out = +-((norm * level) / s).  A wavefront owns 1024
+// consecutive outputs; lane L decodes elements 256q + 4L .. +3 (q = 0..3),
+// so every 16-byte store instruction of the wave writes 1 KiB of
+// consecutive memory.  Lanes 2m and 2m+1 read the two halves of one nibble
+// word.  All loads of a lane are issued before any arithmetic (indices past
+// n are clamped to element 0 and their results dropped).  Pow2: d is a
+// power of two >= 4, so the 4 elements of a group share one bucket and the
+// bucket index is a shift.
 template <bool Pow2, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_kernel(
     const float *__restrict__ norms, const uint32_t *__restrict__ nib, uint64_t n, uint32_t d,
     uint32_t dshift, uint32_t s, float *__restrict__ out)
 {
     const float sf = (float)s;
-    const uint64_t ngroups = (n + 3) >> 2;
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t gi = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < ngroups;
-         gi += stride) {
-        const uint64_t e = gi << 2;
-        const uint32_t word = ld<NT>(nib + (e >> 3));
-        const uint32_t h = (gi & 1u) ? (word & 0xFFFFu) : (word >> 16);
-        float o[4];
-        if constexpr (Pow2) {
-            const float norm = norms[e >> dshift];
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
+    const uint64_t wstride = (uint64_t)gridDim.x * kBlockWaves;
+    for (uint64_t t = (uint64_t)blockIdx.x * kBlockWaves + threadIdx.x / kWave; t < ntiles;
+         t += wstride) {
+        uint64_t e[4];
+        uint32_t word[4];
+        float nrm[4][4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t nb = (h >> (12 - 4 * q)) & 0xFu;
-                const float m = (norm * (float)(nb & 7u)) / sf;
-                o[q] = (nb & 8u) ? -m : m;
-            }
-        } else {
+        for (int q = 0; q < 4; ++q) {
+            e[q] = t * kWaveElems + 256u * q + 4u * lane;
+            const uint64_t es = e[q] < n ? e[q] : 0;
+            word[q] = ld<NT>(nib + (es >> 3));
+            if constexpr (Pow2) {
+                nrm[q][0] = norms[es >> dshift];
+            } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint64_t ei = e + q < n ? e + q : e;
-                const uint32_t nb = (h >> (12 - 4 * q)) & 0xFu;
-                const float m = (norms[ei / d] * (float)(nb & 7u)) / sf;
-                o[q] = (nb & 8u) ? -m : m;
+                for (int j = 0; j < 4; ++j)
+                    nrm[q][j] = norms[(es + j < n ? es + j : es) / d];
             }
         }
-        if (e + 4 <= n) {
-            v4f x;
-            x.x = o[0];
-            x.y = o[1];
-            x.z = o[2];
-            x.w = o[3];
-            st<NT>(reinterpret_cast<v4f *>(out + e), x);
-        } else {
-            for (int q = 0; q < 4; ++q)
-                if (e + q < n)
-                    out[e + q] = o[q];
+        float o[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t h = (lane & 1u) ? (word[q] & 0xFFFFu) : (word[q] >> 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t nb = (h >> (12 - 4 * j)) & 0xFu;
+                const float m = (Pow2 ? nrm[q][0] : nrm[q][j]) * (float)(nb & 7u);
+                const float v = m / sf;
+                o[q][j] = (nb & 8u) ? -v : v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (e[q] + 4 <= n) {
+                v4f x;
+                x.x = o[q][0];
+                x.y = o[q][1];
+                x.z = o[q][2];
+                x.w = o[q][3];
+                st<NT>(reinterpret_cast<v4f *>(out + e[q]), x);
+            } else {
+                for (int j = 0; j < 4; ++j)
+                    if (e[q] + j < n)
+                        out[e[q] + j] = o[q][j];
+            }
         }
     }
 }
@@ -284,13 +358,19 @@ hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t
         nb_done = n / d;
         if (nb_done) {
             const uint32_t grid = grid_for((nb_done + kBlockWaves - 1) / kBlockWaves, 0);
-#define GCQ_FUSED(CC)                                                                              \
-    if (tu.qsgd_nt)                                                                                     \
-        qsgd_fused_kernel<CC, true><<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms,     \
-                                                                         nibbles, nb_done);      \
-    else                                                                                           \
-        qsgd_fused_kernel<CC, false><<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms,    \
-                                                                          nibbles, nb_done);
+#define GCQ_FUSED(CC)                                                                  \
+    if (tu.qsgd_nt && tu.qsgd_rcp)                                                     \
+        qsgd_fused_kernel<CC, true, true><<<grid, kBlockThreads, 0, stream>>>(         \
+            g, s, k0, k1, norms, nibbles, nb_done);                                    \
+    else if (tu.qsgd_nt)                                                               \
+        qsgd_fused_kernel<CC, true, false><<<grid, kBlockThreads, 0, stream>>>(        \
+            g, s, k0, k1, norms, nibbles, nb_done);                                    \
+    else if (tu.qsgd_rcp)                                                              \
+        qsgd_fused_kernel<CC, false, true><<<grid, kBlockThreads, 0, stream>>>(        \
+            g, s, k0, k1, norms, nibbles, nb_done);                                    \
+    else                                                                               \
+        qsgd_fused_kernel<CC, false, false><<<grid, kBlockThreads, 0, stream>>>(       \
+            g, s, k0, k1, norms, nibbles, nb_done);
             switch (C) {
             case 1: GCQ_FUSED(1) break;
             case 2: GCQ_FUSED(2) break;
@@ -335,21 +415,25 @@ hipError_t launch_qsgd_dequant(const float *norms, const uint32_t *nibbles, uint
     if (!n)
         return hipSuccess;
     const gcq_tuning tu = tuning();
-    const uint64_t ngroups = (n + 3) >> 2;
-    const uint32_t grid = grid_for((ngroups + kBlockThreads - 1) / kBlockThreads, 0);
+    const uint64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
+    const uint32_t grid = grid_for((ntiles + kBlockWaves - 1) / kBlockWaves, 0);
     const bool pow2 = d >= 4 && (d & (d - 1)) == 0;
     const uint32_t dshift = pow2 ? (uint32_t)__builtin_ctz(d) : 0u;
+#define GCQ_DQ(P, NT)                                                                           \
+    qsgd_dequant_kernel<P, NT><<<grid, kBlockThreads, 0, stream>>>(norms, nibbles, n, d, dshift, s, \
+                                                                   out)
     if (pow2) {
-        if (tu.qsgd_nt)
-            qsgd_dequant_kernel<true, true><<<grid, kBlockThreads, 0, stream>>>(norms, nibbles, n, d,
-                                                                                dshift, s, out);
+        if (tu.qsgd_dequant_nt)
+            GCQ_DQ(true, true);
         else
-            qsgd_dequant_kernel<true, false><<<grid, kBlockThreads, 0, stream>>>(
-                norms, nibbles, n, d, dshift, s, out);
+            GCQ_DQ(true, false);
     } else {
-        qsgd_dequant_kernel<false, false><<<grid, kBlockThreads, 0, stream>>>(norms, nibbles, n, d,
-                                                                              dshift, s, out);
+        if (tu.qsgd_dequant_nt)
+            GCQ_DQ(false, true);
+        else
+            GCQ_DQ(false, false);
     }
+#undef GCQ_DQ
     return hipGetLastError();
 }
 

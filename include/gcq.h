@@ -222,8 +222,11 @@ typedef struct gcq_tuning {
                               16-byte pieces side by side and each quad of
                               lanes assembles four packed words (default);
                               1: each lane owns a 64-byte run of 16 elements */
-    int gc2_nt;            /* 1: non-temporal hints on the quantizer's loads and
-                              stores (default 1) */
+    int gc2_nt;            /* non-temporal hints in the 2-bit quantizer, a mask:
+                              1 g loads, 2 r loads, 4 r stores, 8 packed-word
+                              stores (default 7: all but the packed words);
+                              layout 1 treats any
+                              non-zero mask as 15 */
     int gc2_blocks_per_cu; /* 0: one 4096-element tile per workgroup (default);
                               k > 0: k workgroups per compute unit, grid-stride */
     int dq_nt_loads;       /* 1: non-temporal loads of the packed words in
@@ -235,21 +238,32 @@ typedef struct gcq_tuning {
                               consecutive sums directly */
     int dq_blocks_per_cu;  /* 0: one packed word position per thread (default);
                               k > 0: k workgroups per compute unit, grid-stride */
-    int qsgd_nt;           /* 1: non-temporal hints in the QSGD kernels */
+    int dq_fp4_decode;     /* 1: decode two codes per instruction with the FP4
+                              conversion (default); 0: one signed-byte
+                              conversion per code */
+    int qsgd_nt;           /* 1: non-temporal hints in the QSGD quantizer */
+    int qsgd_rcp;          /* 1: division-free level arithmetic in the QSGD
+                              quantizer that provably reproduces the results of
+                              the per-element IEEE division, with an exact
+                              fallback where it cannot (default); 0: one IEEE
+                              division per element */
+    int qsgd_dequant_nt;   /* 1: non-temporal hints in qsgd_dequant */
 } gcq_tuning;
 
 /*
  * gcq_get_tuning -- copy the current knobs into *out (host struct).  The
  * initial values are the library defaults, overridden by the environment
  * variables GCQ_GC2_LAYOUT, GCQ_GC2_NT, GCQ_GC2_BLOCKS_PER_CU,
- * GCQ_DQ_NT_LOADS, GCQ_DQ_NT_STORES, GCQ_DQ_LDS_STORES,
- * GCQ_DQ_BLOCKS_PER_CU and GCQ_QSGD_NT when set.
+ * GCQ_DQ_NT_LOADS, GCQ_DQ_NT_STORES, GCQ_DQ_LDS_STORES, GCQ_DQ_FP4_DECODE,
+ * GCQ_DQ_BLOCKS_PER_CU, GCQ_QSGD_NT, GCQ_QSGD_RCP and GCQ_QSGD_DEQUANT_NT when
+ * set.
  * Errors: GCQ_ERR_NULL.
  *
  * gcq_set_tuning -- replace the knobs with *t (host struct).  Takes effect
  * for calls made after it returns; it must not run concurrently with
  * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
- * flag not 0/1, a layout not 0/1, a block count outside 0..1024); on error
+ * flag not 0/1, gc2_nt outside 0..15, a layout not 0/1, a block count
+ * outside 0..1024); on error
  * nothing changes.
  */
 int gcq_get_tuning(gcq_tuning *out);

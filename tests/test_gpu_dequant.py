@@ -43,9 +43,11 @@ def test_config3_w16(gpu):
     assert np.array_equal(bits(host(acc_d)), bits(acc_h))
 
 
-DQ_VARIANTS = [dict(dq_nt_loads=l, dq_nt_stores=s, dq_lds_stores=d, dq_blocks_per_cu=b)
-               for (l, s, d, b) in [(1, 0, 1, 0), (1, 0, 0, 0), (0, 1, 1, 4), (0, 0, 0, 2),
-                                    (1, 1, 0, 0), (0, 0, 1, 1), (1, 1, 1, 8), (0, 1, 0, 0)]]
+DQ_VARIANTS = [dict(dq_nt_loads=l, dq_nt_stores=s, dq_lds_stores=d, dq_blocks_per_cu=b,
+                    dq_fp4_decode=f)
+               for (l, s, d, b, f) in [(1, 1, 1, 0, 1), (1, 0, 0, 0, 1), (0, 1, 1, 4, 0),
+                                       (0, 0, 0, 2, 1), (1, 1, 0, 0, 0), (0, 0, 1, 1, 1),
+                                       (1, 1, 1, 8, 0), (0, 1, 0, 0, 1)]]
 
 
 @pytest.mark.parametrize("var", range(len(DQ_VARIANTS)))

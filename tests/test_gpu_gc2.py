@@ -36,10 +36,12 @@ def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-VARIANTS = [dict(gc2_layout=0, gc2_nt=1, gc2_blocks_per_cu=0),
-            dict(gc2_layout=1, gc2_nt=1, gc2_blocks_per_cu=0),
+VARIANTS = [dict(gc2_layout=0, gc2_nt=15, gc2_blocks_per_cu=0),
+            dict(gc2_layout=1, gc2_nt=15, gc2_blocks_per_cu=0),
             dict(gc2_layout=0, gc2_nt=0, gc2_blocks_per_cu=8),
-            dict(gc2_layout=1, gc2_nt=0, gc2_blocks_per_cu=2)]
+            dict(gc2_layout=1, gc2_nt=0, gc2_blocks_per_cu=2),
+            dict(gc2_layout=0, gc2_nt=5, gc2_blocks_per_cu=0),
+            dict(gc2_layout=0, gc2_nt=10, gc2_blocks_per_cu=3)]
 
 
 @pytest.fixture

@@ -56,9 +56,19 @@ def check_case(gpu, g, d, s, seed):
     return norms, nib, out, want_norms, want_out
 
 
-def test_config4(gpu):
+@pytest.fixture
+def knobs(gpu):
+    old = gpu.get_tuning()
+    yield gpu
+    gpu.set_tuning(**old)
+
+
+@pytest.mark.parametrize("rcp,nt,dnt", [(1, 0, 1), (0, 1, 0), (1, 1, 0)])
+def test_config4(knobs, rcp, nt, dnt):
+    gpu = knobs
+    gpu.set_tuning(qsgd_rcp=rcp, qsgd_nt=nt, qsgd_dequant_nt=dnt)
     cfg = wl.CONFIGS[4]
-    say("qsgd config 4", cfg.n)
+    say("qsgd config 4", cfg.n, "rcp", rcp, "nt", nt)
     g = wl.gradient(cfg, 0)
     norms, nib, out, want_norms, want_out = check_case(gpu, g, cfg.d, cfg.s, wl.qsgd_seed(0))
     assert norms.size == 119_338 and nib.size == 7_637_605
@@ -78,8 +88,11 @@ def test_bucket_sizes_ragged(gpu, d):
         check_case(gpu, g, d, s, int(rs.integers(1 << 62)))
 
 
-def test_all_levels_and_special_values(gpu):
-    say("qsgd spiky + specials")
+@pytest.mark.parametrize("rcp", [1, 0])
+def test_all_levels_and_special_values(knobs, rcp):
+    gpu = knobs
+    gpu.set_tuning(qsgd_rcp=rcp)
+    say("qsgd spiky + specials, rcp", rcp)
     g = wl.qsgd_spiky(512 * 300, 512, 5)
     g[512 * 10:512 * 11] = 0.0                 # zero bucket
     g[512 * 11:512 * 12] = -0.0
@@ -91,6 +104,29 @@ def test_all_levels_and_special_values(gpu):
     k = np.arange(g.size)
     lv = (nib[k // 8] >> (28 - 4 * (k % 8)).astype(np.uint32)) & 7
     assert set(np.unique(lv)) == set(range(8))
+
+
+# j1^2 + j2^2 + j3^2 = s^2: entries (j/s) N have norm N and x = j exactly
+PYTHAGOREAN = {3: (1, 2, 2), 5: (0, 3, 4), 6: (2, 4, 4), 7: (2, 3, 6)}
+
+
+@pytest.mark.parametrize("s", [3, 5, 6, 7])
+def test_levels_near_integer_boundaries(gpu, s):
+    # buckets whose few non-zero entries put x on, or a few ulps beside, the
+    # level boundaries x = j: the division-free level path must hand these
+    # to the exact path and agree with it bit for bit
+    say("qsgd near-boundary levels, s", s)
+    rs = np.random.default_rng(s)
+    nb, d = 2000, 512
+    g = np.zeros(nb * d, np.float32)
+    for b in range(nb):
+        N = rs.uniform(1, 2) * 10.0 ** rs.integers(-30, 30)
+        vals = np.array([j / s * N for j in PYTHAGOREAN[s]], np.float32)
+        ulps = rs.integers(-3, 4, 3).astype(np.int32)
+        vals = (vals.view(np.int32) + np.where(vals != 0, ulps, 0)).view(np.float32)
+        pos = rs.choice(d, 3, replace=False)
+        g[b * d + pos] = vals * np.where(rs.random(3) < 0.5, -1, 1).astype(np.float32)
+    check_case(gpu, g, d, s, 1234 + s)
 
 
 def test_probability_zero_step_at_u_zero(gpu):
