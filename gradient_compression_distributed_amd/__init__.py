@@ -38,7 +38,7 @@ class GcqError(RuntimeError):
 class Tuning(ctypes.Structure):
     """Mirror of ``gcq_tuning`` (launch knobs; results never depend on them)."""
     _fields_ = [(f, ctypes.c_int) for f in (
-        "gc2_layout", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
+        "gc2_unroll", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
         "dq_lds_stores", "dq_blocks_per_cu", "dq_fp4_decode", "qsgd_nt", "qsgd_rcp",
         "qsgd_dequant_nt")]
 

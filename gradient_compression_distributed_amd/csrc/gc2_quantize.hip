@@ -36,7 +36,7 @@ __device__ __forceinline__ float gc2_residual(float v, uint32_t code, float t)
 
 // Non-temporal hints per operand (a bit mask): g loads, r loads, r stores,
 // packed-word stores.
-constexpr int kNtG = 1, kNtR = 2, kNtRStore = 4, kNtOut = 8, kNtAll = 15;
+constexpr int kNtG = 1, kNtR = 2, kNtRStore = 4, kNtOut = 8;
 
 // Four elements -> their residuals (stored) and one byte of codes, first
 // element in the top bit pair.
@@ -55,70 +55,56 @@ __device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
     return (c0 << 6) | (c1 << 4) | (c2 << 2) | c3;
 }
 
-// Full wave tile, layout 0.  Lane L loads elements 256k + 4L .. +3 of the
-// tile for k = 0..3, so every dwordx4 load of the wave covers 1 KiB of
-// consecutive memory.  Those four elements are byte (L % 4) of packed word
-// 16k + L/4 (byte 0 = most significant).  A quad of lanes therefore holds
-// the four bytes of four words; one DPP broadcast per source lane lets lane
-// 4m + j assemble word 16j + m, so the wave stores its 64 words as one
-// 256-byte block.
-template <int NT>
-__device__ __forceinline__ void gc2_tile_coalesced(const GCQ_GLOBAL float *__restrict__ g,
-                                                   GCQ_GLOBAL float *__restrict__ r,
-                                                   GCQ_GLOBAL uint32_t *__restrict__ out, float t,
-                                                   uint32_t lane)
+// Full wave tile of 256*U elements (U = 1, 2 or 4 float4 per stream per
+// lane).  Lane L loads elements 256k + 4L .. +3 of the tile for k < U, so
+// every dwordx4 load of the wave covers 1 KiB of consecutive memory.  Those
+// four elements are byte (L % 4) of packed word 16k + L/4 (byte 0 = most
+// significant).  A quad of lanes therefore holds the four bytes of U words;
+// one DPP broadcast per source lane lets lane 4m + j (j < U) assemble word
+// 16j + m, so the wave stores its 16U words as U runs of 64 bytes.
+//
+// The tile size sets how far apart the in-flight accesses of the chip lie:
+// with one float4 per lane (U = 1) a workgroup touches 4 KiB per stream and
+// the resident workgroups cover one compact window of each buffer, which
+// streams faster on HBM3E than four float4 per lane.
+template <int U, int NT>
+__device__ __forceinline__ void gc2_wave_tile(const GCQ_GLOBAL float *__restrict__ g,
+                                              GCQ_GLOBAL float *__restrict__ r,
+                                              GCQ_GLOBAL uint32_t *__restrict__ out, float t,
+                                              uint32_t lane)
 {
     const GCQ_GLOBAL v4f *g4 = (const GCQ_GLOBAL v4f *)g;
     GCQ_GLOBAL v4f *r4 = (GCQ_GLOBAL v4f *)r;
-    v4f gv[4], rv[4];
+    v4f gv[U], rv[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < U; ++k) {
         gv[k] = ld<(NT & kNtG) != 0>(g4 + k * kWave + lane);
         rv[k] = ld<(NT & kNtR) != 0>(r4 + k * kWave + lane);
     }
     uint32_t bytes = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < U; ++k)
         bytes |= gc2_quad<NT>(gv[k], rv[k], t, r4 + k * kWave + lane) << (8 * k);
     const uint32_t x0 = dev::dpp<dev::kQuadBcast0>(bytes), x1 = dev::dpp<dev::kQuadBcast1>(bytes);
     const uint32_t x2 = dev::dpp<dev::kQuadBcast2>(bytes), x3 = dev::dpp<dev::kQuadBcast3>(bytes);
     const uint32_t j = lane & 3u, sh = 8u * j;
     const uint32_t word = (((x0 >> sh) & 0xFFu) << 24) | (((x1 >> sh) & 0xFFu) << 16) |
                           (((x2 >> sh) & 0xFFu) << 8) | ((x3 >> sh) & 0xFFu);
-    st<(NT & kNtOut) != 0>(out + 16u * j + (lane >> 2), word);
+    if (U == 4 || j < (uint32_t)U)
+        st<(NT & kNtOut) != 0>(out + 16u * j + (lane >> 2), word);
 }
 
-// Full wave tile, layout 1: lane L owns elements 16L .. 16L+15 (a 64-byte
-// run, four dwordx4 loads 64 bytes apart across lanes) and packs its own
-// word with no cross-lane traffic.
-template <int NT>
-__device__ __forceinline__ void gc2_tile_runs(const GCQ_GLOBAL float *__restrict__ g,
-                                              GCQ_GLOBAL float *__restrict__ r,
-                                              GCQ_GLOBAL uint32_t *__restrict__ out, float t,
-                                              uint32_t lane)
-{
-    const GCQ_GLOBAL v4f *g4 = (const GCQ_GLOBAL v4f *)g + 4u * lane;
-    GCQ_GLOBAL v4f *r4 = (GCQ_GLOBAL v4f *)r + 4u * lane;
-    v4f gv[4], rv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        gv[k] = ld<(NT & kNtG) != 0>(g4 + k);
-        rv[k] = ld<(NT & kNtR) != 0>(r4 + k);
-    }
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        word |= gc2_quad<NT>(gv[k], rv[k], t, r4 + k) << (24 - 8 * k);
-    st<(NT & kNtOut) != 0>(out + lane, word);
-}
-
-// Wave tile that runs past the end of its bucket: lane L packs word
-// (e0/16 + L) element by element with bounds checks; pairs past n stay 00.
+// Wave tile of 256*U elements that runs past the end of its bucket: lane
+// L < 16U packs word (e0/16 + L) element by element with bounds checks;
+// pairs past n stay 00.
+template <int U>
 __device__ __forceinline__ void gc2_tile_partial(const GCQ_GLOBAL float *__restrict__ g,
                                                  GCQ_GLOBAL float *__restrict__ r,
                                                  GCQ_GLOBAL uint32_t *__restrict__ out, uint64_t n,
                                                  uint64_t e0, float t, uint32_t lane)
 {
+    if (lane >= 16u * U)
+        return;
     const uint64_t w = (e0 >> 4) + lane;
     const uint64_t base = w << 4;
     if (base >= n)
@@ -158,16 +144,18 @@ __device__ __forceinline__ uint32_t gc2_find_bucket(const Gc2Desc *__restrict__ 
 
 // One kernel for the single-buffer call (Table = false: the descriptor is a
 // kernel argument) and the fused multi-bucket call (Table = true: a device
-// table of buckets, each owning a contiguous range of block tiles).  The
-// block -> tile map is a grid-stride loop; with a grid of one block per
-// tile (the default) it runs once.  A block tile is 16 KiB-aligned within
-// its bucket, so no cache line is shared between workgroups, and thus
-// between the XCDs' L2 caches.
-template <int Layout, int NT, bool Table>
+// table of buckets, each owning a contiguous range of block tiles of
+// 1024*U elements).  The block -> tile map is a grid-stride loop; with a
+// grid of one block per tile (the default) it runs once, and tiles are
+// handed out in address order.  A block tile is 4U KiB-aligned within its
+// bucket, so no cache line of a bucket is shared between workgroups, and
+// thus between the XCDs' L2 caches.
+template <int U, int NT, bool Table>
 __global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
     Gc2Desc one, const Gc2Desc *__restrict__ table, uint32_t nbuckets, uint64_t total_tiles,
     uint32_t tiles_per_bucket)
 {
+    constexpr uint64_t kWaveTile = 256u * U, kBlockTile = kWaveTile * kBlockWaves;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = threadIdx.x / kWave;
     uint64_t tile = blockIdx.x;
@@ -191,74 +179,76 @@ __global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
         const GCQ_GLOBAL float *g = (const GCQ_GLOBAL float *)d.g;
         GCQ_GLOBAL float *r = (GCQ_GLOBAL float *)d.r;
         GCQ_GLOBAL uint32_t *out = (GCQ_GLOBAL uint32_t *)d.out;
-        const uint64_t e0 = (tile - d.tile_begin) * kTileElems + (uint64_t)wave * kWaveElems;
-        if (e0 + kWaveElems <= d.n) {
-            if constexpr (Layout == 0)
-                gc2_tile_coalesced<NT>(g + e0, r + e0, out + (e0 >> 4), d.t, lane);
-            else
-                gc2_tile_runs<NT>(g + e0, r + e0, out + (e0 >> 4), d.t, lane);
-        } else if (e0 < d.n) {
-            gc2_tile_partial(g, r, out, d.n, e0, d.t, lane);
-        }
+        const uint64_t e0 = (tile - d.tile_begin) * kBlockTile + (uint64_t)wave * kWaveTile;
+        if (e0 + kWaveTile <= d.n)
+            gc2_wave_tile<U, NT>(g + e0, r + e0, out + (e0 >> 4), d.t, lane);
+        else if (e0 < d.n)
+            gc2_tile_partial<U>(g, r, out, d.n, e0, d.t, lane);
     }
 }
 
-template <bool Table>
-hipError_t launch(const Gc2Desc &one, const Gc2Desc *table, uint32_t nb, uint64_t total_tiles,
-                  uint32_t tpb, hipStream_t stream)
+template <int U, bool Table>
+void launch_nt(int nt, uint32_t grid, const Gc2Desc &one, const Gc2Desc *table, uint32_t nb,
+               uint64_t total_tiles, uint32_t tpb, hipStream_t stream)
 {
-    const gcq_tuning tu = tuning();
-    const uint32_t grid = grid_for(total_tiles, tu.gc2_blocks_per_cu);
     const dim3 block(kBlockThreads);
-#define GCQ_GC2(L, NT) \
-    gc2_quantize_kernel<L, NT, Table><<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb)
-    if (tu.gc2_layout == 1) {
-        // layout 1 only in the all / none forms
-        if (tu.gc2_nt)
-            GCQ_GC2(1, kNtAll);
-        else
-            GCQ_GC2(1, 0);
-    } else {
-        switch (tu.gc2_nt) {
-        case 0: GCQ_GC2(0, 0); break;
-        case 1: GCQ_GC2(0, 1); break;
-        case 2: GCQ_GC2(0, 2); break;
-        case 3: GCQ_GC2(0, 3); break;
-        case 4: GCQ_GC2(0, 4); break;
-        case 5: GCQ_GC2(0, 5); break;
-        case 6: GCQ_GC2(0, 6); break;
-        case 7: GCQ_GC2(0, 7); break;
-        case 8: GCQ_GC2(0, 8); break;
-        case 9: GCQ_GC2(0, 9); break;
-        case 10: GCQ_GC2(0, 10); break;
-        case 11: GCQ_GC2(0, 11); break;
-        case 12: GCQ_GC2(0, 12); break;
-        case 13: GCQ_GC2(0, 13); break;
-        case 14: GCQ_GC2(0, 14); break;
-        default: GCQ_GC2(0, 15); break;
-        }
+#define GCQ_GC2(NT) \
+    gc2_quantize_kernel<U, NT, Table><<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb)
+    switch (nt) {
+    case 0: GCQ_GC2(0); break;
+    case 1: GCQ_GC2(1); break;
+    case 2: GCQ_GC2(2); break;
+    case 3: GCQ_GC2(3); break;
+    case 4: GCQ_GC2(4); break;
+    case 5: GCQ_GC2(5); break;
+    case 6: GCQ_GC2(6); break;
+    case 7: GCQ_GC2(7); break;
+    case 8: GCQ_GC2(8); break;
+    case 9: GCQ_GC2(9); break;
+    case 10: GCQ_GC2(10); break;
+    case 11: GCQ_GC2(11); break;
+    case 12: GCQ_GC2(12); break;
+    case 13: GCQ_GC2(13); break;
+    case 14: GCQ_GC2(14); break;
+    default: GCQ_GC2(15); break;
     }
 #undef GCQ_GC2
+}
+
+template <bool Table>
+hipError_t launch(const gcq_tuning &tu, const Gc2Desc &one, const Gc2Desc *table, uint32_t nb,
+                  uint64_t total_tiles, uint32_t tpb, hipStream_t stream)
+{
+    const uint32_t grid = grid_for(total_tiles, tu.gc2_blocks_per_cu);
+    switch (tu.gc2_unroll) {
+    case 1: launch_nt<1, Table>(tu.gc2_nt, grid, one, table, nb, total_tiles, tpb, stream); break;
+    case 2: launch_nt<2, Table>(tu.gc2_nt, grid, one, table, nb, total_tiles, tpb, stream); break;
+    default: launch_nt<4, Table>(tu.gc2_nt, grid, one, table, nb, total_tiles, tpb, stream); break;
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
+uint64_t gc2_tile_elems(const gcq_tuning &tu) { return 1024u * (uint64_t)tu.gc2_unroll; }
+
 hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream)
 {
-    const uint64_t tiles = (one.n + kTileElems - 1) / kTileElems;
+    const gcq_tuning tu = tuning();
+    const uint64_t te = gc2_tile_elems(tu);
+    const uint64_t tiles = (one.n + te - 1) / te;
     if (!tiles)
         return hipSuccess;
-    return launch<false>(one, nullptr, 1, tiles, 0, stream);
+    return launch<false>(tu, one, nullptr, 1, tiles, 0, stream);
 }
 
-hipError_t launch_gc2_table(const Gc2Desc *dev_table, uint32_t nbuckets, uint64_t total_tiles,
-                            uint32_t tiles_per_bucket, hipStream_t stream)
+hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint32_t nbuckets,
+                            uint64_t total_tiles, uint32_t tiles_per_bucket, hipStream_t stream)
 {
     if (!total_tiles || !nbuckets)
         return hipSuccess;
     Gc2Desc none = {};
-    return launch<true>(none, dev_table, nbuckets, total_tiles, tiles_per_bucket, stream);
+    return launch<true>(tu, none, dev_table, nbuckets, total_tiles, tiles_per_bucket, stream);
 }
 
 }  // namespace gcq

@@ -198,13 +198,15 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
     uint64_t total_tiles = 0;
     // every bucket spanning the same number of tiles lets the kernel find a
     // tile's bucket by one division
-    uint64_t tpb = (buckets[0].n + gcq::kTileElems - 1) / gcq::kTileElems;
+    const gcq_tuning tu = gcq::tuning();
+    const uint64_t te = gcq::gc2_tile_elems(tu);
+    uint64_t tpb = (buckets[0].n + te - 1) / te;
     for (uint32_t b = 0; b < num_buckets; ++b) {
         const gc2_bucket &k = buckets[b];
         int st = check_gc2(k.g, k.r, k.n, k.t, k.out_words, &ranges);
         if (st != GCQ_OK)
             return st;
-        const uint64_t tiles = (k.n + gcq::kTileElems - 1) / gcq::kTileElems;
+        const uint64_t tiles = (k.n + te - 1) / te;
         if (tiles != tpb)
             tpb = 0;
         total_tiles += tiles;
@@ -224,7 +226,7 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
     for (uint32_t b = 0; b < num_buckets; ++b) {
         const gc2_bucket &k = buckets[b];
         descs[b] = Gc2Desc{k.g, k.r, k.out_words, (uint64_t)k.n, tile, k.t, 0};
-        tile += (k.n + gcq::kTileElems - 1) / gcq::kTileElems;
+        tile += (k.n + te - 1) / te;
     }
     const size_t bytes = num_buckets * sizeof(Gc2Desc);
     hipStream_t hs = (hipStream_t)stream;
@@ -263,7 +265,7 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         sp = &s;
     }
     Slot &s = *sp;
-    hipError_t e = gcq::launch_gc2_table(s.dev, num_buckets, total_tiles, (uint32_t)tpb, hs);
+    hipError_t e = gcq::launch_gc2_table(tu, s.dev, num_buckets, total_tiles, (uint32_t)tpb, hs);
     if (e != hipSuccess)
         return launch_status(e);
     if (hipEventRecord(s.ev, hs) != hipSuccess)

@@ -10,14 +10,14 @@
 
 namespace gcq {
 
-// Geometry of the 2-bit quantizer.  A wavefront (64 lanes) owns a "wave
-// tile" of 1024 consecutive elements = 64 packed words, one word per lane
-// on the way out; a 256-thread workgroup owns a block tile of 4 wave tiles.
+// Launch geometry: 64-lane wavefronts in 256-thread workgroups.  A "wave
+// tile" of 1024 elements (one float4 per lane in each of four 1 KiB runs)
+// is the unit of the QSGD kernels; the 2-bit quantizer's tile size is a
+// launch knob (gc2_tile_elems).
 constexpr int kWave = 64;
 constexpr int kBlockThreads = 256;
 constexpr int kBlockWaves = kBlockThreads / kWave;
 constexpr uint64_t kWaveElems = 1024;
-constexpr uint64_t kTileElems = kWaveElems * kBlockWaves;
 
 // Device-side bucket descriptor of the fused multi-bucket launch.
 struct Gc2Desc {
@@ -50,11 +50,15 @@ int device_cus();
 uint32_t grid_for(uint64_t work_blocks, int blocks_per_cu);
 
 // ---- launchers (return the hipError_t of the launch) -------------------
+// Elements per workgroup tile of the 2-bit quantizer under tuning `tu`
+// (the unit of Gc2Desc::tile_begin).
+uint64_t gc2_tile_elems(const gcq_tuning &tu);
 hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream);
+// `tu` is the tuning the table's tile_begin values were computed with.
 // tiles_per_bucket > 0 when every bucket spans exactly that many tiles
 // (the kernel then finds its bucket by a division instead of a search).
-hipError_t launch_gc2_table(const Gc2Desc *dev_table, uint32_t nbuckets, uint64_t total_tiles,
-                            uint32_t tiles_per_bucket, hipStream_t stream);
+hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint32_t nbuckets,
+                            uint64_t total_tiles, uint32_t tiles_per_bucket, hipStream_t stream);
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t,
                                  float *acc, hipStream_t stream);
 hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t s, uint64_t seed,

@@ -34,7 +34,9 @@ void init_locked()
     if (g_init)
         return;
     // Defaults: the fastest settings measured on MI355X at 2^30 elements.
-    g_tuning.gc2_layout = env_flag("GCQ_GC2_LAYOUT", 0);
+    g_tuning.gc2_unroll = env_int("GCQ_GC2_UNROLL", 1);
+    if (g_tuning.gc2_unroll != 2 && g_tuning.gc2_unroll != 4)
+        g_tuning.gc2_unroll = 1;
     g_tuning.gc2_nt = std::max(0, std::min(15, env_int("GCQ_GC2_NT", 7)));
     g_tuning.gc2_blocks_per_cu = env_count("GCQ_GC2_BLOCKS_PER_CU", 0);
     g_tuning.dq_nt_loads = env_flag("GCQ_DQ_NT_LOADS", 1);
@@ -62,7 +64,7 @@ gcq_tuning tuning()
 
 bool tuning_valid(const gcq_tuning &t)
 {
-    return flag_ok(t.gc2_layout) && t.gc2_nt >= 0 && t.gc2_nt <= 15 && count_ok(t.gc2_blocks_per_cu) &&
+    return (t.gc2_unroll == 1 || t.gc2_unroll == 2 || t.gc2_unroll == 4) && t.gc2_nt >= 0 && t.gc2_nt <= 15 && count_ok(t.gc2_blocks_per_cu) &&
            flag_ok(t.dq_nt_loads) && flag_ok(t.dq_nt_stores) && flag_ok(t.dq_lds_stores) &&
            count_ok(t.dq_blocks_per_cu) && flag_ok(t.dq_fp4_decode) && flag_ok(t.qsgd_nt) &&
            flag_ok(t.qsgd_rcp) && flag_ok(t.qsgd_dequant_nt);

@@ -218,16 +218,15 @@ const char *gcq_status_string(int status);
  * bit-identical outputs; only the time differs.
  */
 typedef struct gcq_tuning {
-    int gc2_layout;        /* 2-bit quantizer lane layout. 0: lanes load
-                              16-byte pieces side by side and each quad of
-                              lanes assembles four packed words (default);
-                              1: each lane owns a 64-byte run of 16 elements */
+    int gc2_unroll;        /* 2-bit quantizer: float4 per lane and stream,
+                              1, 2 or 4.  A workgroup quantizes 1024 * U
+                              consecutive elements of a bucket, each lane U
+                              float4 of g and of r; quads of lanes assemble
+                              the packed words.  Default 1 */
     int gc2_nt;            /* non-temporal hints in the 2-bit quantizer, a mask:
                               1 g loads, 2 r loads, 4 r stores, 8 packed-word
-                              stores (default 7: all but the packed words);
-                              layout 1 treats any
-                              non-zero mask as 15 */
-    int gc2_blocks_per_cu; /* 0: one 4096-element tile per workgroup (default);
+                              stores (default 7: all but the packed words) */
+    int gc2_blocks_per_cu; /* 0: one tile per workgroup (default);
                               k > 0: k workgroups per compute unit, grid-stride */
     int dq_nt_loads;       /* 1: non-temporal loads of the packed words in
                               gc2_dequant_reduce */
@@ -262,8 +261,8 @@ typedef struct gcq_tuning {
  * gcq_set_tuning -- replace the knobs with *t (host struct).  Takes effect
  * for calls made after it returns; it must not run concurrently with
  * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
- * flag not 0/1, gc2_nt outside 0..15, a layout not 0/1, a block count
- * outside 0..1024); on error
+ * flag not 0/1, gc2_nt outside 0..15, gc2_unroll not 1/2/4, a block
+ * count outside 0..1024); on error
  * nothing changes.
  */
 int gcq_get_tuning(gcq_tuning *out);

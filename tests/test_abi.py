@@ -155,10 +155,10 @@ def test_tuning_roundtrip_and_validation(lib):
     t = gcq.Tuning()
     assert lib.gcq_get_tuning(ctypes.byref(t)) == OK
     saved = t.as_dict()
-    assert saved["gc2_layout"] in (0, 1) and saved["gc2_blocks_per_cu"] >= 0
+    assert saved["gc2_unroll"] in (1, 2, 4) and saved["gc2_blocks_per_cu"] >= 0
     assert lib.gcq_get_tuning(None) == E_NULL
     assert lib.gcq_set_tuning(None) == E_NULL
-    for field, bad in [("gc2_layout", 2), ("gc2_nt", -1), ("gc2_nt", 16), ("dq_lds_stores", 5),
+    for field, bad in [("gc2_unroll", 3), ("gc2_unroll", 0), ("gc2_nt", -1), ("gc2_nt", 16), ("dq_lds_stores", 5),
                        ("gc2_blocks_per_cu", 1025), ("dq_blocks_per_cu", -3), ("qsgd_nt", 7),
                        ("qsgd_rcp", 2), ("qsgd_dequant_nt", 3), ("dq_fp4_decode", 2)]:
         b = gcq.Tuning(**saved)

@@ -36,12 +36,12 @@ def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-VARIANTS = [dict(gc2_layout=0, gc2_nt=15, gc2_blocks_per_cu=0),
-            dict(gc2_layout=1, gc2_nt=15, gc2_blocks_per_cu=0),
-            dict(gc2_layout=0, gc2_nt=0, gc2_blocks_per_cu=8),
-            dict(gc2_layout=1, gc2_nt=0, gc2_blocks_per_cu=2),
-            dict(gc2_layout=0, gc2_nt=5, gc2_blocks_per_cu=0),
-            dict(gc2_layout=0, gc2_nt=10, gc2_blocks_per_cu=3)]
+VARIANTS = [dict(gc2_unroll=1, gc2_nt=7, gc2_blocks_per_cu=0),
+            dict(gc2_unroll=2, gc2_nt=15, gc2_blocks_per_cu=0),
+            dict(gc2_unroll=4, gc2_nt=0, gc2_blocks_per_cu=8),
+            dict(gc2_unroll=1, gc2_nt=0, gc2_blocks_per_cu=2),
+            dict(gc2_unroll=4, gc2_nt=5, gc2_blocks_per_cu=0),
+            dict(gc2_unroll=2, gc2_nt=10, gc2_blocks_per_cu=3)]
 
 
 @pytest.fixture
@@ -234,17 +234,19 @@ def test_buckets_fused_equals_per_bucket_and_oracle(default_tuning, var):
             assert np.array_equal(bits(host(rbuf[roff[i]:roff[i] + n])), bits(rs_[i])), (step, i)
 
 
-@pytest.mark.parametrize("var", [0, 2])
+@pytest.mark.parametrize("var", [0, 1, 2])
 def test_buckets_equal_tile_counts(default_tuning, var):
-    # every bucket spans the same number of 4096-element tiles (the kernel
-    # then maps a tile to its bucket by a division), with different n inside
+    # every bucket spans the same number of workgroup tiles (1024 * unroll
+    # elements; the kernel then maps a tile to its bucket by a division),
+    # with different n inside
     import torch
 
     gpu = default_tuning
     gpu.set_tuning(**VARIANTS[var])
     say("gc2 equal-tile buckets variant", VARIANTS[var])
     rs = np.random.default_rng(8 + var)
-    sizes = [8192, 4097, 6000, 8192, 5555, 8191, 4100] * 3
+    te = 1024 * VARIANTS[var]["gc2_unroll"]
+    sizes = [2 * te, te + 1, te + te // 2 + 3, 2 * te, te + te // 3, 2 * te - 1, te + 4] * 3
     t = 0.01
     gs = [(rs.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
     r_h = [np.zeros(n, np.float32) for n in sizes]
