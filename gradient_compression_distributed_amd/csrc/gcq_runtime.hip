@@ -47,6 +47,8 @@ void init_locked()
     g_tuning.qsgd_nt = env_flag("GCQ_QSGD_NT", 0);
     g_tuning.qsgd_rcp = env_flag("GCQ_QSGD_RCP", 1);
     g_tuning.qsgd_dequant_nt = env_flag("GCQ_QSGD_DEQUANT_NT", 1);
+    g_tuning.qsgd_blocks_per_cu = env_count("GCQ_QSGD_BLOCKS_PER_CU", 32);
+    g_tuning.qsgd_dequant_blocks_per_cu = env_count("GCQ_QSGD_DEQUANT_BLOCKS_PER_CU", 0);
     g_init = true;
 }
 
@@ -67,7 +69,8 @@ bool tuning_valid(const gcq_tuning &t)
     return (t.gc2_unroll == 1 || t.gc2_unroll == 2 || t.gc2_unroll == 4) && t.gc2_nt >= 0 && t.gc2_nt <= 15 && count_ok(t.gc2_blocks_per_cu) &&
            flag_ok(t.dq_nt_loads) && flag_ok(t.dq_nt_stores) && flag_ok(t.dq_lds_stores) &&
            count_ok(t.dq_blocks_per_cu) && flag_ok(t.dq_fp4_decode) && flag_ok(t.qsgd_nt) &&
-           flag_ok(t.qsgd_rcp) && flag_ok(t.qsgd_dequant_nt);
+           flag_ok(t.qsgd_rcp) && flag_ok(t.qsgd_dequant_nt) && count_ok(t.qsgd_blocks_per_cu) &&
+           count_ok(t.qsgd_dequant_blocks_per_cu);
 }
 
 void set_tuning(const gcq_tuning &t)

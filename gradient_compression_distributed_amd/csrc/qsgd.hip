@@ -55,6 +55,16 @@ __device__ __forceinline__ void uniforms4(uint64_t q, uint32_t k0, uint32_t k1, 
         u[j] = (float)(c[j] >> 8) * 0x1p-24f;
 }
 
+// The same draws as integers U = u 2^24 (exact floats below 2^24).
+__device__ __forceinline__ void uniforms4_int(uint64_t q, uint32_t k0, uint32_t k1, float (&U)[4])
+{
+    uint32_t c[4] = {(uint32_t)q, (uint32_t)(q >> 32), 0u, 0u};
+    philox4x32_10(c, k0, k1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        U[j] = (float)(c[j] >> 8);
+}
+
 // Level of one element (Knowl 1), exactly as defined: a = |g|/norm (one
 // correctly rounded division), x = a s, l = floor(x), level l+1 when
 // u < x - l; zero norm -> 0; x >= s -> s; NaN -> 0.
@@ -75,29 +85,65 @@ __device__ __forceinline__ uint32_t qsgd_level_exact(float gabs, float norm, flo
     return level;
 }
 
-// The same level without a division per element.  For a bucket norm in
-// [2^-120, 2^120], x' = |g| * rs with rs = RN(RN(1/norm) * s) differs from
-// the exact x = RN(RN(|g|/norm) * s) by less than 40 * 2^-24 < 2^-18.6 (five
-// relative roundings of at most 2^-24 each on a value below 7.0001, since
-// |g| <= norm up to its own rounding; all intermediates are normal
-// whenever x' > 2^-18).  So when no integer and no u lies within
-// kGuard = 2^-18 of x', floor and the comparison with u come out the same
-// as for the exact x.  That also settles the clamp at s: x' <= s (1 + 2^-22)
-// < s + kGuard, so an x' near s is near an integer.  g == 0 is exact
-// (x' = x = 0).  `safe` is false for the lanes (a few per million) that
-// must take the exact path.
+// The same level without a division per element.  With l = floor(x) and
+// p = x - l, the level l + [u < p] equals ceil(x - u) in exact arithmetic
+// (u in [0, 1); the integer case x - u = l is p = u, level l).  The kernel
+// computes d = RN(x' - u) with x' = RN(|g| * rs), rs = RN(RN(1/norm) * s),
+// and u = U 2^-24 folded into one fma.  For a bucket norm in
+// [2^-120, 2^120], x' differs from the exact x = RN(RN(|g|/norm) * s) by
+// less than 40 * 2^-24 (five relative roundings of at most 2^-24 each on a
+// value below 7.0001, since |g| <= norm up to its own rounding), and the
+// subtraction adds at most 2^-22 (half an ulp below 8): |d - (x - u)| <
+// 44 * 2^-24 < kGuard = 2^-18.  So whenever d lies more than kGuard from
+// every integer, ceil(d) = ceil(x - u), the exact level.  That covers the
+// clamp at s too: x <= s (1 + 3 * 2^-24), so x - u lies within kGuard of s
+// or below s - kGuard whenever x >= s, and ceil gives s or the lane falls
+// back.  The shortcut only runs for finite buckets (a NaN or Inf element
+// makes the norm NaN or Inf, outside the range), so d is finite.
 constexpr float kGuard = 0x1p-18f;
+// kGuard < f < 1 - kGuard for f = ceil(d) - d, as one comparison of
+// |f - 0.5|; its rounding is monotone and 0.5 - kGuard is a float, so it
+// only ever errs towards "unsafe".
+constexpr float kSafeDist = 0.5f - kGuard;
 
-__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, float u, bool &safe)
+// Level from the shortcut; `dist` = |f - 0.5|, safe when below kSafeDist.
+__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, float U, float &dist)
 {
-    const float x = gabs * rs;               // <= 7.001: the conversion stays in range
-    const float l = floorf(x);
-    const float p = x - l;                   // exact
-    safe = gabs == 0.0f || (p > kGuard && p < 1.0f - kGuard && fabsf(u - p) > kGuard);
-    return (uint32_t)l + (u < p ? 1u : 0u);
+    const float d = __builtin_fmaf(U, -0x1p-24f, gabs * rs);
+    const float c = __builtin_ceilf(d);
+    dist = __builtin_fabsf((c - d) - 0.5f);
+    return (uint32_t)c;                      // c in [-0, s + 1]: in range
 }
 
 __device__ __forceinline__ uint32_t sign_bit(float gv) { return gv < 0.0f ? 8u : 0u; }
+
+// 16 bits of nibbles for four elements, first element in the top nibble:
+// nibble = sign << 3 | level, sign = [g < 0].  pack4_exact tests g < 0 per
+// element.  pack4 takes the sign bits from the bit patterns of g + 0.0
+// (which turns -0.0 into +0.0, so the sign bit is set exactly when g < 0,
+// NaNs aside: callers route NaNs to pack4_exact): the top bytes of g0 and
+// g2 go to bytes 1 and 0 of one word, those of g1 and g3 to another, which
+// is then shifted down by a nibble.
+__device__ __forceinline__ uint32_t pack4_exact(const float (&gq)[4], const uint32_t (&lv)[4])
+{
+    uint32_t h = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        h |= (sign_bit(gq[q]) | lv[q]) << (12 - 4 * q);
+    return h;
+}
+
+__device__ __forceinline__ uint32_t pack4(const float (&gq)[4], const uint32_t (&lv)[4])
+{
+    const uint32_t a = __builtin_amdgcn_perm(__float_as_uint(gq[0] + 0.0f),
+                                             __float_as_uint(gq[2] + 0.0f), 0x0C0C0703u);
+    const uint32_t b = __builtin_amdgcn_perm(__float_as_uint(gq[1] + 0.0f),
+                                             __float_as_uint(gq[3] + 0.0f), 0x0C0C0703u);
+    uint32_t h = (((((lv[0] << 4) | lv[1]) << 4) | lv[2]) << 4) | lv[3];
+    h |= a & 0x8080u;
+    h |= (b >> 4) & 0x0808u;
+    return h;
+}
 
 // A bucket takes the division-free level path when its norm is in this
 // range (false for 0, Inf and NaN norms, which take the exact path).
@@ -146,10 +192,10 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
             v[c] = ld<NT>(reinterpret_cast<const v4f *>(g + base + 256u * c) + lane);
         // the draws do not depend on the norm: computing them first overlaps
         // the Philox arithmetic with the latency of the wave reduction
-        float u[C][4];
+        float U[C][4];
 #pragma unroll
         for (int c = 0; c < C; ++c)
-            uniforms4((base + 256u * c + 4u * lane) >> 2, k0, k1, u[c]);
+            uniforms4_int((base + 256u * c + 4u * lane) >> 2, k0, k1, U[c]);
         double ss = 0.0;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -169,27 +215,29 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
         for (int c = 0; c < C; ++c) {
             const float gq[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
             uint32_t lv[4];
+            bool all_ok = false;
             if (fast) {
-                bool ok[4];
+                float dist[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, u[c][q], ok[q]);
-                if (!(ok[0] && ok[1] && ok[2] && ok[3])) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (!ok[q])
-                            lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, u[c][q]);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, u[c][q]);
+                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[c][q], dist[q]);
+                all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
             }
-            uint32_t hv = 0;
+            if (all_ok) {
+                h[c] = pack4(gq, lv);
+            } else {
+                // rare: redo the group element by element, the exact way
+                // where the shortcut cannot decide
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                hv |= (sign_bit(gq[q]) | lv[q]) << (12 - 4 * q);
-            h[c] = hv;
+                for (int q = 0; q < 4; ++q) {
+                    float dist = 1.0f;
+                    if (fast)
+                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[c][q], dist);
+                    if (!(dist < kSafeDist))
+                        lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, U[c][q] * 0x1p-24f);
+                }
+                h[c] = pack4_exact(gq, lv);
+            }
         }
         uint32_t *out = nib + (base >> 3);
         const bool odd = (lane & 1u) != 0;
@@ -357,7 +405,8 @@ hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t
     if (C == 1 || C == 2 || C == 4 || C == 8) {
         nb_done = n / d;
         if (nb_done) {
-            const uint32_t grid = grid_for((nb_done + kBlockWaves - 1) / kBlockWaves, 0);
+            const uint32_t grid =
+                grid_for((nb_done + kBlockWaves - 1) / kBlockWaves, tu.qsgd_blocks_per_cu);
 #define GCQ_FUSED(CC)                                                                  \
     if (tu.qsgd_nt && tu.qsgd_rcp)                                                     \
         qsgd_fused_kernel<CC, true, true><<<grid, kBlockThreads, 0, stream>>>(         \
@@ -416,7 +465,8 @@ hipError_t launch_qsgd_dequant(const float *norms, const uint32_t *nibbles, uint
         return hipSuccess;
     const gcq_tuning tu = tuning();
     const uint64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
-    const uint32_t grid = grid_for((ntiles + kBlockWaves - 1) / kBlockWaves, 0);
+    const uint32_t grid =
+        grid_for((ntiles + kBlockWaves - 1) / kBlockWaves, tu.qsgd_dequant_blocks_per_cu);
     const bool pow2 = d >= 4 && (d & (d - 1)) == 0;
     const uint32_t dshift = pow2 ? (uint32_t)__builtin_ctz(d) : 0u;
 #define GCQ_DQ(P, NT)                                                                           \

@@ -247,6 +247,13 @@ typedef struct gcq_tuning {
                               fallback where it cannot (default); 0: one IEEE
                               division per element */
     int qsgd_dequant_nt;   /* 1: non-temporal hints in qsgd_dequant */
+    int qsgd_blocks_per_cu; /* fused QSGD quantizer (d a multiple of 256, up to
+                               2048): 0: one wavefront per bucket; k > 0: k
+                               workgroups per compute unit, each wavefront
+                               strides over many buckets (default 32) */
+    int qsgd_dequant_blocks_per_cu; /* qsgd_dequant: 0: one wavefront per
+                               1024 elements; k > 0: k workgroups per compute
+                               unit, grid-stride (default 0) */
 } gcq_tuning;
 
 /*
