@@ -19,6 +19,7 @@ __all__ = [
     "GcqError", "load", "lib_path", "gc2_quantize", "gc2_quantize_buckets",
     "gc2_dequant_reduce", "qsgd_quantize", "qsgd_dequant", "gc2_packed_words",
     "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "get_tuning", "BucketList",
+    "cdsgd_update_quantize", "cdsgd_local_update", "cdsgd_compresses",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +78,10 @@ def load():
     lib.qsgd_quantize.restype = i32
     lib.qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp, vp]
     lib.qsgd_dequant.restype = i32
+    lib.cdsgd_update_quantize.argtypes = [vp, vp, vp, sz, f32, f32, vp, vp]
+    lib.cdsgd_update_quantize.restype = i32
+    lib.cdsgd_local_update.argtypes = [vp, vp, sz, f32, vp]
+    lib.cdsgd_local_update.restype = i32
     lib.gc2_packed_words.argtypes = [sz]
     lib.gc2_packed_words.restype = sz
     lib.qsgd_num_buckets.argtypes = [sz, u32]
@@ -173,6 +178,45 @@ def gc2_quantize(g, r, t: float, out=None):
     _check(lib.gc2_quantize(_ptr(g), _ptr(r), n, ctypes.c_float(t), _ptr(out),
                             _stream(g.device)), "gc2_quantize")
     return out
+
+
+def cdsgd_compresses(count: int, k: int) -> bool:
+    """CD-SGD's k-step switch (Algorithm 1, section 3.2.1): iteration
+    ``count`` compresses its gradient unless ``count % k == 0``, when the
+    full-precision gradient is pushed instead (host logic only)."""
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    return count % k != 0
+
+
+def cdsgd_update_quantize(g, r, w, t: float, eta: float, out=None):
+    """A compressing CD-SGD iteration on one buffer: ``w -= eta * g`` (local
+    update) and one 2-bit quantize step of (g, r); returns the packed words."""
+    import torch
+
+    lib = load()
+    _dev(g, torch.float32, "g")
+    n = g.numel()
+    _dev(r, torch.float32, "r", n)
+    _dev(w, torch.float32, "w", n)
+    if out is None:
+        out = torch.empty(gc2_packed_words(n), dtype=torch.int32, device=g.device)
+    _dev(out, torch.int32, "out", gc2_packed_words(n))
+    _check(lib.cdsgd_update_quantize(_ptr(g), _ptr(r), _ptr(w), n, ctypes.c_float(t),
+                                     ctypes.c_float(eta), _ptr(out), _stream(g.device)),
+           "cdsgd_update_quantize")
+    return out
+
+
+def cdsgd_local_update(g, w, eta: float):
+    """A correction iteration's local update: ``w -= eta * g``."""
+    import torch
+
+    lib = load()
+    _dev(g, torch.float32, "g")
+    _dev(w, torch.float32, "w", g.numel())
+    _check(lib.cdsgd_local_update(_ptr(g), _ptr(w), g.numel(), ctypes.c_float(eta),
+                                  _stream(g.device)), "cdsgd_local_update")
 
 
 class BucketList:

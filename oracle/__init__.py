@@ -13,6 +13,9 @@ passage of the pages it follows:
   "Two bit quantization" and "Format of compressed gradient"; CD-SGD 3.4.1.
 * ``gc2_dequant_reduce`` -- same PR, "Local kvstore" (device 0 dequantizes
   and sums the other devices' packed data), fixed worker order.
+* ``cdsgd_local_update`` / ``cdsgd_update_quantize`` -- CD-SGD 3.4.1
+  eq. (11) (w_loc = w - eta g), 3.2.1 Algorithm 1 and Figure 4(b) (the
+  local update and the compression both read the same gradient).
 * ``qsgd_norms`` / ``qsgd_levels`` / ``qsgd_quantize`` / ``qsgd_dequant``
   -- QSGD summary, Knowl 1 (Q_s), Knowl 2 (norm/sign/level tuple),
   Knowl 8 (bucketing).
@@ -47,6 +50,10 @@ def _load():
     lib.oracle_gc2_quantize.argtypes = [vp, vp, sz, f32, vp]
     lib.oracle_gc2_quantize.restype = None
     lib.oracle_gc2_dequant_reduce.argtypes = [vp, u32, sz, f32, vp]
+    lib.oracle_cdsgd_local_update.argtypes = [vp, vp, sz, f32]
+    lib.oracle_cdsgd_local_update.restype = None
+    lib.oracle_cdsgd_update_quantize.argtypes = [vp, vp, vp, sz, f32, f32, vp]
+    lib.oracle_cdsgd_update_quantize.restype = None
     lib.oracle_gc2_dequant_reduce.restype = None
     lib.oracle_philox4x32_10.argtypes = [vp, vp, vp]
     lib.oracle_philox4x32_10.restype = None
@@ -105,6 +112,34 @@ def gc2_quantize(g: np.ndarray, r: np.ndarray, t: float, out: np.ndarray | None 
     if out.size < packed_words(n):
         raise ValueError("out too small")
     lib.oracle_gc2_quantize(_ptr(g), _ptr(r), n, ctypes.c_float(t), _ptr(out))
+    return out
+
+
+def cdsgd_local_update(g: np.ndarray, w: np.ndarray, eta: float) -> None:
+    """w = w - eta * g in float32 (product, then difference); ``w`` in place."""
+    lib = _load()
+    _f32(g, "g"), _f32(w, "w")
+    if w.size != g.size:
+        raise ValueError("g and w differ in size")
+    lib.oracle_cdsgd_local_update(_ptr(g), _ptr(w), g.size, ctypes.c_float(eta))
+
+
+def cdsgd_update_quantize(g: np.ndarray, r: np.ndarray, w: np.ndarray, t: float, eta: float,
+                          out: np.ndarray | None = None):
+    """Local update of ``w`` and one quantize step of (g, r); returns the
+    packed words, ``r`` and ``w`` are updated in place."""
+    lib = _load()
+    _f32(g, "g"), _f32(r, "r"), _f32(w, "w")
+    n = g.size
+    if r.size != n or w.size != n:
+        raise ValueError("g, r and w differ in size")
+    if out is None:
+        out = np.empty(packed_words(n), dtype=np.uint32)
+    _u32(out, "out")
+    if out.size < packed_words(n):
+        raise ValueError("out too small")
+    lib.oracle_cdsgd_update_quantize(_ptr(g), _ptr(r), _ptr(w), n, ctypes.c_float(t),
+                                     ctypes.c_float(eta), _ptr(out))
     return out
 
 

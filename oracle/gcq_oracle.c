@@ -17,7 +17,9 @@
  *         sections "Two bit quantization", "Format of compressed gradient",
  *         "Local kvstore", "Dist kvstore".
  *   [CD]  "CD-SGD: Distributed Stochastic Gradient Descent with Compression
- *         and Delay Compensation": section 3.4.1 "Update Rules".
+ *         and Delay Compensation": section 3.4.1 "Update Rules" (eq. 10,
+ *         11), section 3.2.1 "Implementation on MXNet" (Algorithm 1, the
+ *         k-step switch) and Figure 4(b) (comm_buf, loc_buf).
  *   [QS]  "QSGD: Communication-Efficient SGD via Gradient Quantization and
  *         Encoding" (chapterpal summary): Knowl 1 (the Q_s operator),
  *         Knowl 2 (the (norm, sign, level) tuple), Knowl 8 (bucketing).
@@ -72,6 +74,38 @@ void oracle_gc2_quantize(const float *g, float *r, size_t n, float t,
         r[i] = v - sent;                /* what was not sent is carried */
         out[i / 16] |= code << (30u - 2u * (unsigned)(i % 16));
     }
+}
+
+/*
+ * [CD] 3.4.1 eq. (11): the local weights for the next iteration are the
+ * pulled global weights minus eta times the local gradient.  [CD] 3.2.1 and
+ * Figure 4(b): loc_buf holds the pulled weights and is updated with the
+ * gradient in comm_buf; in the same iteration the gradient is compressed
+ * (Algorithm 1: when count % k != 0), and both read comm_buf without
+ * modifying it.  Reading taken: the step is the literal w - eta * g in
+ * float32, the product rounded, then the difference rounded (no fused
+ * multiply-add).
+ *
+ * w[n] is read and overwritten; g[n] is only read.
+ */
+void oracle_cdsgd_local_update(const float *g, float *w, size_t n, float eta)
+{
+    for (size_t i = 0; i < n; i++) {
+        float step = eta * g[i];
+        w[i] = w[i] - step;
+    }
+}
+
+/*
+ * A compressing iteration of [CD] Algorithm 1 on one buffer: the local
+ * update of w and the 2-bit quantizer of g with residual r, as two
+ * independent uses of the same gradient.
+ */
+void oracle_cdsgd_update_quantize(const float *g, float *r, float *w, size_t n,
+                                  float t, float eta, uint32_t *out)
+{
+    oracle_cdsgd_local_update(g, w, n, eta);
+    oracle_gc2_quantize(g, r, n, t, out);
 }
 
 /* Value a single 2-bit code stands for ([CD] 3.4.1).  01 is never produced
