@@ -84,6 +84,8 @@ def parse():
                    help="target CPU work of the oracle sample")
     p.add_argument("--no-per-bucket", action="store_true",
                    help="skip the 128-launch comparison of the fused quantizer")
+    p.add_argument("--no-next", action="store_true",
+                   help="skip timing CD-SGD's fused local update + quantize")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 4 GiB device copy (reference kernel for counters)")
     return p.parse_args()
@@ -192,6 +194,40 @@ def main():
         ops["gc2_quantize_buckets"]["fused_speedup"] = round(
             per_bucket_ms / op_ms["gc2_quantize_buckets"], 3)
 
+    # CD-SGD's local update fused with the quantizer (a widening of the path;
+    # timed on its own, outside the step): the fused call, the update alone,
+    # and the update plus the single-buffer quantizer as two launches
+    next_ops = None
+    if not args.no_next:
+        cfg7 = wl.CONFIGS[7]
+        g, wloc = grads[0], qout
+        wl.fill_normal_(wloc, cfg7.cid, 999, cfg7.w_sigma)
+        reps = max(3, K // 2)
+
+        def timed(fn):
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        fused_ms = timed(lambda: gcq.cdsgd_update_quantize(g, r, wloc, cfg7.t, cfg7.eta,
+                                                           out=words[0]))
+        upd_ms = timed(lambda: gcq.cdsgd_local_update(g, wloc, cfg7.eta))
+        quant_ms = timed(lambda: gcq.gc2_quantize(g, r, cfg7.t, out=words[0]))
+        next_ops = {}
+        for name, ms, bpe in (("cdsgd_update_quantize", fused_ms, 20.25),
+                              ("cdsgd_local_update", upd_ms, 12.0)):
+            gbps = bpe * n / (ms / 1e3) / 1e9
+            next_ops[name] = {"ms": round(ms, 4), "elements_per_s": n / (ms / 1e3),
+                              "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                              "bytes_per_element": bpe}
+        next_ops["cdsgd_update_quantize"]["separate_launches_ms"] = round(upd_ms + quant_ms, 4)
+        next_ops["cdsgd_update_quantize"]["config"] = {"eta": cfg7.eta, "t": cfg7.t, "n": n}
+
     copy_gbps = None
     if args.copy_calibration:
         src = grads[0]
@@ -230,6 +266,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": ops,
+        "next_ops": next_ops,
         "gc2_quantize_elements_per_s": ops["gc2_quantize_buckets"]["elements_per_s"],
         "device_copy_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "device": torch.cuda.get_device_name(dev),

@@ -2,7 +2,9 @@
 // residual (MXNet PR "2bit gradient compression": "Two bit quantization",
 // "Format of compressed gradient"; CD-SGD 3.4.1 "Update Rules") for gfx950,
 // single buffer and fused multi-bucket (IMerge-style merged transmission
-// units) launches.
+// units) launches; and CD-SGD's local update of the weights, alone or fused
+// with the quantizer (CD-SGD 3.4.1 eq. (11); 3.2.1 Algorithm 1 and Figure
+// 4(b): both read the same gradient buffer).
 //
 // HBM-bound: per element 4 B of g and 4 B of r are read, 4 B of r and 1/4 B
 // of packed code written (12.25 B), ~10 VALU ops of arithmetic.  No MFMA.
@@ -55,6 +57,15 @@ __device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
     return (c0 << 6) | (c1 << 4) | (c2 << 2) | c3;
 }
 
+// CD-SGD local update of four weights: w - eta * g, the product and the
+// difference each rounded once (no fma: the library is built with
+// -ffp-contract=off).
+__device__ __forceinline__ v4f local_step(v4f w, v4f g, float eta)
+{
+    const v4f step = eta * g;
+    return w - step;
+}
+
 // Full wave tile of 256*U elements (U = 1, 2 or 4 float4 per stream per
 // lane).  Lane L loads elements 256k + 4L .. +3 of the tile for k < U, so
 // every dwordx4 load of the wave covers 1 KiB of consecutive memory.  Those
@@ -67,19 +78,32 @@ __device__ __forceinline__ uint32_t gc2_quad(v4f g, v4f r, float t, RP rout)
 // with one float4 per lane (U = 1) a workgroup touches 4 KiB per stream and
 // the resident workgroups cover one compact window of each buffer, which
 // streams faster on HBM3E than four float4 per lane.
-template <int U, int NT>
+//
+// Loc = true adds CD-SGD's local update: the weights w (same layout, same
+// hints as r) are loaded with g and r and stored updated, so the gradient is
+// read once for both uses.
+template <int U, int NT, bool Loc>
 __device__ __forceinline__ void gc2_wave_tile(const GCQ_GLOBAL float *__restrict__ g,
                                               GCQ_GLOBAL float *__restrict__ r,
                                               GCQ_GLOBAL uint32_t *__restrict__ out, float t,
-                                              uint32_t lane)
+                                              uint32_t lane, GCQ_GLOBAL float *__restrict__ w,
+                                              float eta)
 {
     const GCQ_GLOBAL v4f *g4 = (const GCQ_GLOBAL v4f *)g;
     GCQ_GLOBAL v4f *r4 = (GCQ_GLOBAL v4f *)r;
-    v4f gv[U], rv[U];
+    GCQ_GLOBAL v4f *w4 = (GCQ_GLOBAL v4f *)w;
+    v4f gv[U], rv[U], wv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
         gv[k] = ld<(NT & kNtG) != 0>(g4 + k * kWave + lane);
         rv[k] = ld<(NT & kNtR) != 0>(r4 + k * kWave + lane);
+        if constexpr (Loc)
+            wv[k] = ld<(NT & kNtR) != 0>(w4 + k * kWave + lane);
+    }
+    if constexpr (Loc) {
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            st<(NT & kNtRStore) != 0>(w4 + k * kWave + lane, local_step(wv[k], gv[k], eta));
     }
     uint32_t bytes = 0;
 #pragma unroll
@@ -97,11 +121,12 @@ __device__ __forceinline__ void gc2_wave_tile(const GCQ_GLOBAL float *__restrict
 // Wave tile of 256*U elements that runs past the end of its bucket: lane
 // L < 16U packs word (e0/16 + L) element by element with bounds checks;
 // pairs past n stay 00.
-template <int U>
+template <int U, bool Loc>
 __device__ __forceinline__ void gc2_tile_partial(const GCQ_GLOBAL float *__restrict__ g,
                                                  GCQ_GLOBAL float *__restrict__ r,
                                                  GCQ_GLOBAL uint32_t *__restrict__ out, uint64_t n,
-                                                 uint64_t e0, float t, uint32_t lane)
+                                                 uint64_t e0, float t, uint32_t lane,
+                                                 GCQ_GLOBAL float *__restrict__ wl, float eta)
 {
     if (lane >= 16u * U)
         return;
@@ -113,6 +138,8 @@ __device__ __forceinline__ void gc2_tile_partial(const GCQ_GLOBAL float *__restr
     for (uint32_t p = 0; p < 16; ++p) {
         const uint64_t e = base + p;
         if (e < n) {
+            if constexpr (Loc)
+                wl[e] = wl[e] - eta * g[e];
             const float v = g[e] + r[e];
             const uint32_t c = gc2_code(v, t);
             r[e] = gc2_residual(v, c, t);
@@ -150,11 +177,15 @@ __device__ __forceinline__ uint32_t gc2_find_bucket(const Gc2Desc *__restrict__ 
 // handed out in address order.  A block tile is 4U KiB-aligned within its
 // bucket, so no cache line of a bucket is shared between workgroups, and
 // thus between the XCDs' L2 caches.
-template <int U, int NT, bool Table>
+//
+// Loc = true (single buffer only) is CD-SGD's compressing iteration: the
+// local update of w is fused in (w and eta are unused otherwise).
+template <int U, int NT, bool Table, bool Loc>
 __global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
     Gc2Desc one, const Gc2Desc *__restrict__ table, uint32_t nbuckets, uint64_t total_tiles,
-    uint32_t tiles_per_bucket)
+    uint32_t tiles_per_bucket, float *__restrict__ wloc, float eta)
 {
+    static_assert(!(Table && Loc), "the local update is single-buffer");
     constexpr uint64_t kWaveTile = 256u * U, kBlockTile = kWaveTile * kBlockWaves;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = threadIdx.x / kWave;
@@ -180,10 +211,12 @@ __global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
         GCQ_GLOBAL float *r = (GCQ_GLOBAL float *)d.r;
         GCQ_GLOBAL uint32_t *out = (GCQ_GLOBAL uint32_t *)d.out;
         const uint64_t e0 = (tile - d.tile_begin) * kBlockTile + (uint64_t)wave * kWaveTile;
+        GCQ_GLOBAL float *w = (GCQ_GLOBAL float *)wloc;
         if (e0 + kWaveTile <= d.n)
-            gc2_wave_tile<U, NT>(g + e0, r + e0, out + (e0 >> 4), d.t, lane);
+            gc2_wave_tile<U, NT, Loc>(g + e0, r + e0, out + (e0 >> 4), d.t, lane,
+                                      Loc ? w + e0 : w, eta);
         else if (e0 < d.n)
-            gc2_tile_partial<U>(g, r, out, d.n, e0, d.t, lane);
+            gc2_tile_partial<U, Loc>(g, r, out, d.n, e0, d.t, lane, w, eta);
     }
 }
 
@@ -192,8 +225,9 @@ void launch_nt(int nt, uint32_t grid, const Gc2Desc &one, const Gc2Desc *table, 
                uint64_t total_tiles, uint32_t tpb, hipStream_t stream)
 {
     const dim3 block(kBlockThreads);
-#define GCQ_GC2(NT) \
-    gc2_quantize_kernel<U, NT, Table><<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb)
+#define GCQ_GC2(NT)                                                                            \
+    gc2_quantize_kernel<U, NT, Table, false>                                                   \
+        <<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb, nullptr, 0.0f)
     switch (nt) {
     case 0: GCQ_GC2(0); break;
     case 1: GCQ_GC2(1); break;
@@ -228,6 +262,67 @@ hipError_t launch(const gcq_tuning &tu, const Gc2Desc &one, const Gc2Desc *table
     return hipGetLastError();
 }
 
+// CD-SGD local update alone (a correction iteration): w - eta * g over
+// wave tiles of 256*U elements, lane L owning float4 k*64 + L (k < U).
+template <int U, int NT>
+__global__ __launch_bounds__(kBlockThreads) void local_update_kernel(const float *__restrict__ g,
+                                                                      float *__restrict__ w,
+                                                                      uint64_t n, uint64_t tiles,
+                                                                      float eta)
+{
+    constexpr uint64_t kWaveTile = 256u * U, kBlockTile = kWaveTile * kBlockWaves;
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = threadIdx.x / kWave;
+    const GCQ_GLOBAL float *gg = (const GCQ_GLOBAL float *)g;
+    GCQ_GLOBAL float *ww = (GCQ_GLOBAL float *)w;
+    for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const uint64_t e0 = tile * kBlockTile + (uint64_t)wave * kWaveTile;
+        if (e0 + kWaveTile <= n) {
+            const GCQ_GLOBAL v4f *g4 = (const GCQ_GLOBAL v4f *)(gg + e0);
+            GCQ_GLOBAL v4f *w4 = (GCQ_GLOBAL v4f *)(ww + e0);
+            v4f gv[U], wv[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                gv[k] = ld<(NT & kNtG) != 0>(g4 + k * kWave + lane);
+                wv[k] = ld<(NT & kNtR) != 0>(w4 + k * kWave + lane);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                st<(NT & kNtRStore) != 0>(w4 + k * kWave + lane, local_step(wv[k], gv[k], eta));
+        } else if (e0 < n) {
+            for (uint64_t e = e0 + lane; e < n && e < e0 + kWaveTile; e += kWave)
+                ww[e] = ww[e] - eta * gg[e];
+        }
+    }
+}
+
+// The CD-SGD launches take the quantizer's unroll and block-count knobs,
+// and its non-temporal mask reduced to none (0), all (15) or the default
+// set (g, r and w loads, r and w stores: 7).
+template <int U, int NT>
+void launch_cdsgd_u(bool quant, uint32_t grid, const Gc2Desc &one, float *w, float eta,
+                    uint64_t tiles, hipStream_t stream)
+{
+    if (quant)
+        gc2_quantize_kernel<U, NT, false, true>
+            <<<grid, kBlockThreads, 0, stream>>>(one, nullptr, 1, tiles, 0, w, eta);
+    else
+        local_update_kernel<U, NT>
+            <<<grid, kBlockThreads, 0, stream>>>(one.g, w, one.n, tiles, eta);
+}
+
+template <int U>
+void launch_cdsgd_nt(int nt, bool quant, uint32_t grid, const Gc2Desc &one, float *w, float eta,
+                     uint64_t tiles, hipStream_t stream)
+{
+    if (nt == 0)
+        launch_cdsgd_u<U, 0>(quant, grid, one, w, eta, tiles, stream);
+    else if (nt == 15)
+        launch_cdsgd_u<U, 15>(quant, grid, one, w, eta, tiles, stream);
+    else
+        launch_cdsgd_u<U, 7>(quant, grid, one, w, eta, tiles, stream);
+}
+
 }  // namespace
 
 uint64_t gc2_tile_elems(const gcq_tuning &tu) { return 1024u * (uint64_t)tu.gc2_unroll; }
@@ -240,6 +335,24 @@ hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream)
     if (!tiles)
         return hipSuccess;
     return launch<false>(tu, one, nullptr, 1, tiles, 0, stream);
+}
+
+hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint64_t n, float t,
+                        float eta, bool quant, hipStream_t stream)
+{
+    const gcq_tuning tu = tuning();
+    const uint64_t te = gc2_tile_elems(tu);
+    const uint64_t tiles = (n + te - 1) / te;
+    if (!tiles)
+        return hipSuccess;
+    const Gc2Desc one = {g, r, out, n, 0, t, 0};
+    const uint32_t grid = grid_for(tiles, tu.gc2_blocks_per_cu);
+    switch (tu.gc2_unroll) {
+    case 1: launch_cdsgd_nt<1>(tu.gc2_nt, quant, grid, one, w, eta, tiles, stream); break;
+    case 2: launch_cdsgd_nt<2>(tu.gc2_nt, quant, grid, one, w, eta, tiles, stream); break;
+    default: launch_cdsgd_nt<4>(tu.gc2_nt, quant, grid, one, w, eta, tiles, stream); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint32_t nbuckets,

@@ -49,6 +49,8 @@ bool any_write_overlap(std::vector<Range> &rs)
 
 bool valid_threshold(float t) { return isfinite(t) && t > 0.0f; }
 
+bool valid_rate(float eta) { return isfinite(eta) && eta >= 0.0f; }
+
 constexpr size_t kMaxElems = ((size_t)1 << 62);  // keeps every byte count in range
 
 int check_gc2(const float *g, const float *r, size_t n, float t, const uint32_t *out,
@@ -272,6 +274,45 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         return GCQ_ERR_LAUNCH;
     s.pending = true;
     return GCQ_OK;
+}
+
+int cdsgd_update_quantize(const float *g, float *r, float *w_loc, size_t n, float t, float eta,
+                          uint32_t *out_words, void *stream)
+{
+    std::vector<Range> ranges;
+    int st = check_gc2(g, r, n, t, out_words, &ranges);
+    if (st != GCQ_OK)
+        return st;
+    if (!valid_rate(eta))
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!w_loc)
+        return GCQ_ERR_NULL;
+    if (!aligned(w_loc, 16))
+        return GCQ_ERR_ALIGN;
+    ranges.push_back(range(w_loc, n * 4, true));
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(
+        gcq::launch_cdsgd(g, r, w_loc, out_words, n, t, eta, true, (hipStream_t)stream));
+}
+
+int cdsgd_local_update(const float *g, float *w_loc, size_t n, float eta, void *stream)
+{
+    if (!valid_rate(eta) || n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!g || !w_loc)
+        return GCQ_ERR_NULL;
+    if (!aligned(g, 16) || !aligned(w_loc, 16))
+        return GCQ_ERR_ALIGN;
+    std::vector<Range> ranges = {range(g, n * 4, false), range(w_loc, n * 4, true)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(gcq::launch_cdsgd(g, nullptr, w_loc, nullptr, n, 1.0f, eta, false,
+                                           (hipStream_t)stream));
 }
 
 int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t, float *acc,

@@ -59,6 +59,9 @@ hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream);
 // (the kernel then finds its bucket by a division instead of a search).
 hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint32_t nbuckets,
                             uint64_t total_tiles, uint32_t tiles_per_bucket, hipStream_t stream);
+// CD-SGD local update (Quant = false) or update fused with the quantizer.
+hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint64_t n, float t,
+                        float eta, bool quant, hipStream_t stream);
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t,
                                  float *acc, hipStream_t stream);
 hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t s, uint64_t seed,

@@ -21,6 +21,11 @@ stand-ins for the pages' settings:
    ~ N(0, 0.01^2); d = 512, s = 7; one hash seed per step.
 5. Fused buckets: 2^30 elements in 128 buckets of 8,388,608, sigma_b
    log-uniform in [1e-5, 1e-2] per bucket, t = 1e-3, 5 steps.
+6. CD-SGD local update + quantize on a gradient drawn like config 2's
+   (25,557,032 elements, blocked sigmas in [1e-4, 1e-1], t = 0.01): initial local weights
+   ~ N(0, 0.05^2), local learning rate 0.1 and k-step 2 (CD-SGD section 4,
+   ResNet-50 on ImageNet), 4 iterations.
+7. The same at 2^30 elements with config 5's gradient layout (t = 1e-3).
 """
 from __future__ import annotations
 
@@ -51,6 +56,9 @@ class Config:
     workers: int = 1
     d: int = 0
     s: int = 0
+    eta: float = 0.0         # CD-SGD local learning rate
+    k: int = 0               # CD-SGD k-step
+    w_sigma: float = 0.0     # spread of the initial local weights
 
 
 CONFIGS = {
@@ -61,7 +69,14 @@ CONFIGS = {
     4: Config(4, "QSGD stochastic quantize+dequantize", 61_100_840, sigma=0.01, d=512, s=7),
     5: Config(5, "fused-bucket gc2 quantize+residual, 1G elements", 1 << 30, t=1e-3, steps=5,
               block=8_388_608, sigma_lo=1e-5, sigma_hi=1e-2),
+    6: Config(6, "CD-SGD local update + gc2 quantize, ResNet-50-sized", 25_557_032, t=0.01,
+              steps=4, block=1_048_576, sigma_lo=1e-4, sigma_hi=1e-1, eta=0.1, k=2,
+              w_sigma=0.05),
+    7: Config(7, "CD-SGD local update + gc2 quantize, 1G elements", 1 << 30, t=1e-3, steps=5,
+              block=8_388_608, sigma_lo=1e-5, sigma_hi=1e-2, eta=0.1, k=2, w_sigma=0.05),
 }
+
+WEIGHT_STREAM = 0xFFFFFFE  # the "step" slot of the initial-weight stream
 
 
 def block_sigmas(cfg: Config) -> np.ndarray:
@@ -97,6 +112,11 @@ def gradient_block(cfg: Config, step: int, b: int) -> np.ndarray:
     lo = b * cfg.block
     hi = min(lo + cfg.block, cfg.n)
     return normal_block(cfg.cid, step, b, hi - lo, sig[b])
+
+
+def initial_weights(cfg: Config) -> np.ndarray:
+    """Initial local weights of a CD-SGD config, N(0, w_sigma^2)."""
+    return normal_block(cfg.cid, WEIGHT_STREAM, 0, cfg.n, cfg.w_sigma)
 
 
 def iid_field_words(gen: np.random.Generator, nwords: int, p11: float = 0.05,
@@ -176,6 +196,15 @@ def fill_bucketed_normal_(out, cfg: Config, step: int):
         seg = out[lo:hi]
         seg.normal_(0.0, 1.0, generator=gen)
         seg.mul_(sig[b])
+    return out
+
+
+def fill_normal_(out, cfg_id: int, stream: int, sigma: float):
+    """Fill a device float32 tensor with N(0, sigma^2) from the config's
+    device stream `stream`."""
+    gen = device_generator(cfg_id, stream, out.device)
+    out.normal_(0.0, 1.0, generator=gen)
+    out.mul_(sigma)
     return out
 
 

@@ -9,7 +9,9 @@
  *     threshold takes effect on later calls).
  *   - "CD-SGD: Distributed Stochastic Gradient Descent with Compression and
  *     Delay Compensation": 3.4.1 "Update Rules" (a code that passes the
- *     threshold is worth the threshold itself).
+ *     threshold is worth the threshold itself; eq. (11), the local update),
+ *     3.2.1 Algorithm 1 and Figure 4(b) (the local update and the
+ *     compression read the same gradient buffer).
  *   - "QSGD: Communication-Efficient SGD via Gradient Quantization and
  *     Encoding" (chapterpal summary): Knowl 1 (Q_s), Knowl 2 (the
  *     (norm, sign, level) tuple), Knowl 3 (encode, broadcast, decode),
@@ -138,6 +140,53 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
  */
 int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t,
                        float *acc, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* CD-SGD: local update fused with the 2-bit quantizer                 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * cdsgd_update_quantize -- a compressing iteration of CD-SGD's worker
+ * (Algorithm 1 in 3.2.1: count % k != 0) on one buffer.  Figure 4(b): the
+ * local weights in loc_buf are updated with the gradient in comm_buf, and
+ * the same gradient is compressed; eq. (11) of 3.4.1: the next local
+ * weights are the pulled global weights minus eta times the gradient.
+ * One pass reads g once; for every i < n, in float32:
+ *     w_loc[i] = w_loc[i] - (eta * g[i])     (product rounded, then the
+ *                                              difference; no fused multiply-add)
+ * and exactly gc2_quantize's step on (g[i], r[i]) into out_words.
+ *
+ *   g          in,     float32[n], 16-byte aligned (comm_buf; not modified)
+ *   r          in/out, float32[n], 16-byte aligned (residual)
+ *   w_loc      in/out, float32[n], 16-byte aligned (loc_buf: holds the pulled
+ *              weights on entry, the next local weights on return)
+ *   n          element count (any value)
+ *   t          threshold, finite and > 0
+ *   eta        local learning rate, finite and >= 0
+ *   out_words  out,    uint32[ceil(n/16)], 4-byte aligned
+ *   stream     hipStream_t
+ *
+ * Errors: GCQ_ERR_NULL, GCQ_ERR_THRESHOLD, GCQ_ERR_PARAM (eta), GCQ_ERR_ALIGN,
+ * GCQ_ERR_OVERLAP (g, r, w_loc and out_words pairwise disjoint),
+ * GCQ_ERR_LAUNCH.
+ */
+int cdsgd_update_quantize(const float *g, float *r, float *w_loc, size_t n, float t, float eta,
+                          uint32_t *out_words, void *stream);
+
+/*
+ * cdsgd_local_update -- the local update alone, for CD-SGD's uncompressed
+ * correction iterations (Algorithm 1: count % k == 0, when the full-precision
+ * gradient is pushed): w_loc[i] = w_loc[i] - (eta * g[i]) as above.  The
+ * residual is not touched.
+ *
+ *   g      in,     float32[n], 16-byte aligned
+ *   w_loc  in/out, float32[n], 16-byte aligned
+ *   eta    finite and >= 0
+ *
+ * Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM, GCQ_ERR_ALIGN, GCQ_ERR_OVERLAP,
+ * GCQ_ERR_LAUNCH.
+ */
+int cdsgd_local_update(const float *g, float *w_loc, size_t n, float eta, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* QSGD: bucketed s-level stochastic quantizer                         */

@@ -102,6 +102,33 @@ def test_gc2_buckets_validation(lib):
     assert call([(0, 0, 0, 0, 0.5), (0, 0, 0, 0, 0.5)]) == OK
 
 
+def test_cdsgd_validation(lib):
+    n = 1000
+    g, r, w, o = A, A + (1 << 20), A + (2 << 20), A + (3 << 20)
+    q = lambda g_, r_, w_, n_, t_, e_, o_: lib.cdsgd_update_quantize(
+        vp(g_), vp(r_), vp(w_), n_, F(t_), F(e_), vp(o_), NULL)
+    assert q(g, r, 0, n, 0.5, 0.1, o) == E_NULL
+    assert q(0, r, w, n, 0.5, 0.1, o) == E_NULL
+    assert q(g, r, w, n, 0.0, 0.1, o) == E_THR
+    for bad in (-0.1, float("nan"), float("inf")):
+        assert q(g, r, w, n, 0.5, bad, o) == E_PARAM
+        assert q(g, r, w, 0, 0.5, bad, o) == E_PARAM        # checked even for n == 0
+    assert q(g, r, w, 0, 0.5, 0.1, o) == OK                 # n == 0 is a no-op
+    assert q(g, r, w + 4, n, 0.5, 0.1, o) == E_ALIGN
+    assert q(g, r, g, n, 0.5, 0.1, o) == E_OVERLAP          # w aliases comm_buf
+    assert q(g, r, r + 64, n, 0.5, 0.1, o) == E_OVERLAP     # w inside r
+    assert q(g, r, w, n, 0.5, 0.1, w + 128) == E_OVERLAP    # words over w
+    u = lambda g_, w_, n_, e_: lib.cdsgd_local_update(vp(g_), vp(w_), n_, F(e_), NULL)
+    assert u(g, 0, n, 0.1) == E_NULL
+    assert u(0, w, n, 0.1) == E_NULL
+    assert u(g, w, n, -1.0) == E_PARAM
+    assert u(g, w, 0, float("nan")) == E_PARAM
+    assert u(g, w, 0, 0.1) == OK
+    assert u(g + 8, w, n, 0.1) == E_ALIGN
+    assert u(g, w + 4, n, 0.1) == E_ALIGN
+    assert u(g, g + 16, n, 0.1) == E_OVERLAP
+
+
 def test_dequant_reduce_validation(lib):
     n = 4096
     ws = (ctypes.c_void_p * 3)(A, A + (1 << 20), A + (2 << 20))
