@@ -19,6 +19,9 @@ passage of the pages it follows:
 * ``qsgd_norms`` / ``qsgd_levels`` / ``qsgd_quantize`` / ``qsgd_dequant``
   -- QSGD summary, Knowl 1 (Q_s), Knowl 2 (norm/sign/level tuple),
   Knowl 8 (bucketing).
+* ``qsgd_maxnorms`` / ``qsgd_quantize_maxnorm`` -- Knowl 8, max-norm
+  scaling; ``qsgd_dequant_average`` -- Knowl 3 (decode every peer's message
+  and average).
 * ``philox4x32_10`` / ``uniform`` -- the SC'11 Philox-4x32 generator.  The
   pages name no random source, so the exact uniform stream is
   "parity unpinned" by the pages; it is pinned only statistically.
@@ -66,6 +69,12 @@ def _load():
     lib.oracle_qsgd_quantize.argtypes = [vp, sz, u32, u32, u64, vp, vp]
     lib.oracle_qsgd_quantize.restype = None
     lib.oracle_qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp]
+    lib.oracle_qsgd_maxnorms.argtypes = [vp, sz, u32, vp]
+    lib.oracle_qsgd_maxnorms.restype = None
+    lib.oracle_qsgd_quantize_maxnorm.argtypes = [vp, sz, u32, u32, u64, vp, vp]
+    lib.oracle_qsgd_quantize_maxnorm.restype = None
+    lib.oracle_qsgd_dequant_average.argtypes = [vp, vp, u32, sz, u32, u32, vp]
+    lib.oracle_qsgd_dequant_average.restype = None
     lib.oracle_qsgd_dequant.restype = None
     _lib = lib
     return lib
@@ -217,4 +226,43 @@ def qsgd_dequant(norms: np.ndarray, nibbles: np.ndarray, n: int, d: int, s: int)
         raise ValueError("inputs too small")
     out = np.empty(n, dtype=np.float32)
     lib.oracle_qsgd_dequant(_ptr(norms), _ptr(nibbles), n, d, s, _ptr(out))
+    return out
+
+
+def qsgd_maxnorms(g: np.ndarray, d: int) -> np.ndarray:
+    lib = _load()
+    _f32(g, "g")
+    scales = np.empty(num_buckets(g.size, d), dtype=np.float32)
+    lib.oracle_qsgd_maxnorms(_ptr(g), g.size, d, _ptr(scales))
+    return scales
+
+
+def qsgd_quantize_maxnorm(g: np.ndarray, d: int, s: int, seed: int):
+    lib = _load()
+    _f32(g, "g")
+    scales = np.empty(num_buckets(g.size, d), dtype=np.float32)
+    nib = np.empty(nibble_words(g.size), dtype=np.uint32)
+    lib.oracle_qsgd_quantize_maxnorm(_ptr(g), g.size, d, s, ctypes.c_uint64(seed),
+                                     _ptr(scales), _ptr(nib))
+    return scales, nib
+
+
+def qsgd_dequant_average(scales: list, nibbles: list, n: int, d: int, s: int) -> np.ndarray:
+    """Mean over K workers of the decoded messages (worker order 0..K-1)."""
+    lib = _load()
+    K = len(scales)
+    if K == 0 or len(nibbles) != K:
+        raise ValueError("need K >= 1 scale and nibble arrays")
+    for a in scales:
+        _f32(a, "scales")
+        if a.size < num_buckets(n, d):
+            raise ValueError("scales too small")
+    for a in nibbles:
+        _u32(a, "nibbles")
+        if a.size < nibble_words(n):
+            raise ValueError("nibbles too small")
+    sp = (ctypes.c_void_p * K)(*[_ptr(a) for a in scales])
+    npp = (ctypes.c_void_p * K)(*[_ptr(a) for a in nibbles])
+    out = np.empty(n, dtype=np.float32)
+    lib.oracle_qsgd_dequant_average(sp, npp, K, n, d, s, _ptr(out))
     return out

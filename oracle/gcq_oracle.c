@@ -22,7 +22,8 @@
  *         k-step switch) and Figure 4(b) (comm_buf, loc_buf).
  *   [QS]  "QSGD: Communication-Efficient SGD via Gradient Quantization and
  *         Encoding" (chapterpal summary): Knowl 1 (the Q_s operator),
- *         Knowl 2 (the (norm, sign, level) tuple), Knowl 8 (bucketing).
+ *         Knowl 2 (the (norm, sign, level) tuple), Knowl 3 (decode and
+ *         average), Knowl 8 (bucketing, max-norm scaling).
  *   [PH]  Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *         1, 2, 3" (SC'11): the Philox-4x32 counter-based generator.  The
  *         pages name no random source; this generator is a frozen choice,
@@ -295,5 +296,64 @@ void oracle_qsgd_dequant(const float *norms, const uint32_t *nibbles,
         float m = norms[i / d] * level;
         m = m / sf;
         out[i] = sign ? -m : m;
+    }
+}
+
+/*
+ * [QS] Knowl 8, max-norm scaling: a bucket is scaled by its largest
+ * coordinate magnitude instead of its L2 norm.  The maximum is exact.
+ * Reading taken for NaN: an element takes part only when its magnitude
+ * compares greater than the running maximum, so NaNs never become the scale
+ * (and, as with any scale, quantize to level 0).  scales[ceil(n/d)].
+ */
+void oracle_qsgd_maxnorms(const float *g, size_t n, uint32_t d, float *scales)
+{
+    size_t nb = (n + d - 1) / d;
+    for (size_t b = 0; b < nb; b++) {
+        size_t lo = b * (size_t)d;
+        size_t hi = lo + d < n ? lo + d : n;
+        float m = 0.0f;
+        for (size_t i = lo; i < hi; i++) {
+            float a = fabsf(g[i]);
+            if (a > m)
+                m = a;
+        }
+        scales[b] = m;
+    }
+}
+
+/* Q_s with max-norm bucket scales: the same levels as the L2 quantizer,
+ * given the scales. */
+void oracle_qsgd_quantize_maxnorm(const float *g, size_t n, uint32_t d, uint32_t s,
+                                  uint64_t seed, float *scales, uint32_t *nibbles)
+{
+    oracle_qsgd_maxnorms(g, n, d, scales);
+    oracle_qsgd_levels(g, n, d, s, seed, 0u, scales, nibbles);
+}
+
+/*
+ * [QS] Knowl 3: every processor decodes the messages of all K peers and
+ * averages them, g_bar = (1/K) sum_l Decode(M_l).  Reading taken: for each
+ * element, the K decoded values (each exactly as oracle_qsgd_dequant) are
+ * added in float32 in worker order 0..K-1 starting from +0, and the sum is
+ * divided by K once (correctly rounded).  scales[l] and nibbles[l] are the
+ * l-th worker's bucket scales and nibble words.
+ */
+void oracle_qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibbles,
+                                 uint32_t K, size_t n, uint32_t d, uint32_t s, float *out)
+{
+    const float sf = (float)s;
+    const float kf = (float)K;
+    for (size_t i = 0; i < n; i++) {
+        float acc = 0.0f;
+        for (uint32_t l = 0; l < K; l++) {
+            uint32_t nib = (nibbles[l][i / 8] >> (28u - 4u * (unsigned)(i % 8))) & 15u;
+            uint32_t sign = nib >> 3;
+            float level = (float)(nib & 7u);
+            float m = scales[l][i / d] * level;
+            m = m / sf;
+            acc = acc + (sign ? -m : m);
+        }
+        out[i] = acc / kf;
     }
 }
