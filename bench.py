@@ -228,6 +228,24 @@ def main():
         next_ops["cdsgd_update_quantize"]["separate_launches_ms"] = round(upd_ms + quant_ms, 4)
         next_ops["cdsgd_update_quantize"]["config"] = {"eta": cfg7.eta, "t": cfg7.t, "n": n}
 
+        # QSGD with max-norm bucket scales, and the 16-worker decode-average
+        mx_ms = timed(lambda: gcq.qsgd_quantize_maxnorm(g, QSGD_D, QSGD_S, wl.qsgd_seed(7),
+                                                        scales=norms, nibbles=nib))
+        K = W_WORKERS
+        msgs = [gcq.qsgd_quantize(g, QSGD_D, QSGD_S, wl.qsgd_seed(200 + k)) for k in range(K)]
+        torch.cuda.synchronize()
+        avg_ms = timed(lambda: gcq.qsgd_dequant_average([m[0] for m in msgs], [m[1] for m in msgs],
+                                                        n, QSGD_D, QSGD_S, out=qout))
+        del msgs
+        per_msg = 0.5 + 4.0 / QSGD_D
+        for name, ms, bpe in (("qsgd_quantize_maxnorm", mx_ms, 4.0 + per_msg),
+                              ("qsgd_dequant_average", avg_ms, K * per_msg + 4.0)):
+            gbps = bpe * n / (ms / 1e3) / 1e9
+            next_ops[name] = {"ms": round(ms, 4), "elements_per_s": n / (ms / 1e3),
+                              "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                              "bytes_per_element": round(bpe, 4)}
+        next_ops["qsgd_dequant_average"]["config"] = {"K": K, "d": QSGD_D, "s": QSGD_S, "n": n}
+
     copy_gbps = None
     if args.copy_calibration:
         src = grads[0]

@@ -20,6 +20,7 @@ __all__ = [
     "gc2_dequant_reduce", "qsgd_quantize", "qsgd_dequant", "gc2_packed_words",
     "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "get_tuning", "BucketList",
     "cdsgd_update_quantize", "cdsgd_local_update", "cdsgd_compresses",
+    "qsgd_quantize_maxnorm", "qsgd_dequant_average",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,11 @@ def load():
     lib.qsgd_dequant.restype = i32
     lib.cdsgd_update_quantize.argtypes = [vp, vp, vp, sz, f32, f32, vp, vp]
     lib.cdsgd_update_quantize.restype = i32
+    lib.qsgd_quantize_maxnorm.argtypes = [vp, sz, u32, u32, u64, vp, vp, vp]
+    lib.qsgd_quantize_maxnorm.restype = i32
+    lib.qsgd_dequant_average.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), u32, sz, u32,
+                                         u32, vp, vp]
+    lib.qsgd_dequant_average.restype = i32
     lib.cdsgd_local_update.argtypes = [vp, vp, sz, f32, vp]
     lib.cdsgd_local_update.restype = i32
     lib.gc2_packed_words.argtypes = [sz]
@@ -270,8 +276,9 @@ def gc2_dequant_reduce(words, n: int, t: float, acc=None):
     return acc
 
 
-def qsgd_quantize(g, d: int, s: int, seed: int, norms=None, nibbles=None):
-    """Bucketed QSGD: returns (norms float32[ceil(n/d)], nibbles int32[ceil(n/8)])."""
+def qsgd_quantize(g, d: int, s: int, seed: int, norms=None, nibbles=None, maxnorm: bool = False):
+    """Bucketed QSGD: returns (norms float32[ceil(n/d)], nibbles int32[ceil(n/8)]).
+    With ``maxnorm`` the bucket scale is the largest magnitude (Knowl 8)."""
     import torch
 
     lib = load()
@@ -284,9 +291,36 @@ def qsgd_quantize(g, d: int, s: int, seed: int, norms=None, nibbles=None):
         nibbles = torch.empty(nw, dtype=torch.int32, device=g.device)
     _dev(norms, torch.float32, "norms", nb)
     _dev(nibbles, torch.int32, "nibbles", nw)
-    _check(lib.qsgd_quantize(_ptr(g), n, d, s, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
-                             _ptr(norms), _ptr(nibbles), _stream(g.device)), "qsgd_quantize")
+    fn = lib.qsgd_quantize_maxnorm if maxnorm else lib.qsgd_quantize
+    _check(fn(_ptr(g), n, d, s, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+              _ptr(norms), _ptr(nibbles), _stream(g.device)), "qsgd_quantize")
     return norms, nibbles
+
+
+def qsgd_quantize_maxnorm(g, d: int, s: int, seed: int, scales=None, nibbles=None):
+    """QSGD with max-norm bucket scales: returns (scales, nibbles)."""
+    return qsgd_quantize(g, d, s, seed, norms=scales, nibbles=nibbles, maxnorm=True)
+
+
+def qsgd_dequant_average(scales, nibbles, n: int, d: int, s: int, out=None):
+    """Mean over K workers (order 0..K-1) of their decoded QSGD messages."""
+    import torch
+
+    lib = load()
+    K = len(scales)
+    if K != len(nibbles):
+        raise ValueError("scales and nibbles differ in length")
+    for i in range(K):
+        _dev(scales[i], torch.float32, f"scales[{i}]", qsgd_num_buckets(n, d))
+        _dev(nibbles[i], torch.int32, f"nibbles[{i}]", qsgd_nibble_words(n))
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=scales[0].device)
+    _dev(out, torch.float32, "out", n)
+    sp = (ctypes.c_void_p * max(K, 1))(*[x.data_ptr() for x in scales])
+    npp = (ctypes.c_void_p * max(K, 1))(*[x.data_ptr() for x in nibbles])
+    _check(lib.qsgd_dequant_average(sp, npp, K, n, d, s, _ptr(out), _stream(out.device)),
+           "qsgd_dequant_average")
+    return out
 
 
 def qsgd_dequant(norms, nibbles, n: int, d: int, s: int, out=None):

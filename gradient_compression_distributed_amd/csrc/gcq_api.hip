@@ -348,8 +348,8 @@ int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float
     return launch_status(gcq::launch_dequant_reduce(ws, W, n, t, acc, (hipStream_t)stream));
 }
 
-int qsgd_quantize(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed, float *norms,
-                  uint32_t *nibbles, void *stream)
+static int qsgd_quantize_impl(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed,
+                              float *norms, uint32_t *nibbles, bool maxnorm, void *stream)
 {
     if (d == 0 || s < 1 || s > 7 || n > kMaxElems)
         return GCQ_ERR_PARAM;
@@ -364,8 +364,20 @@ int qsgd_quantize(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t see
                                  range(nibbles, qsgd_nibble_words(n) * 4, true)};
     if (any_write_overlap(ranges))
         return GCQ_ERR_OVERLAP;
-    return launch_status(
-        gcq::launch_qsgd_quantize(g, n, d, s, seed, norms, nibbles, (hipStream_t)stream));
+    return launch_status(gcq::launch_qsgd_quantize(g, n, d, s, seed, norms, nibbles, maxnorm,
+                                                   (hipStream_t)stream));
+}
+
+int qsgd_quantize(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed, float *norms,
+                  uint32_t *nibbles, void *stream)
+{
+    return qsgd_quantize_impl(g, n, d, s, seed, norms, nibbles, false, stream);
+}
+
+int qsgd_quantize_maxnorm(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed,
+                          float *scales, uint32_t *nibbles, void *stream)
+{
+    return qsgd_quantize_impl(g, n, d, s, seed, scales, nibbles, true, stream);
 }
 
 int qsgd_dequant(const float *norms, const uint32_t *nibbles, size_t n, uint32_t d, uint32_t s,
@@ -386,6 +398,36 @@ int qsgd_dequant(const float *norms, const uint32_t *nibbles, size_t n, uint32_t
         return GCQ_ERR_OVERLAP;
     return launch_status(
         gcq::launch_qsgd_dequant(norms, nibbles, n, d, s, out, (hipStream_t)stream));
+}
+
+int qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibbles, uint32_t K,
+                         size_t n, uint32_t d, uint32_t s, float *out, void *stream)
+{
+    if (K == 0 || K > GCQ_MAX_WORKERS || d == 0 || s < 1 || s > 7 || n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!scales || !nibbles || !out)
+        return GCQ_ERR_NULL;
+    if (!aligned(out, 16))
+        return GCQ_ERR_ALIGN;
+    gcq::QsgdMsgs ms;
+    memset(&ms, 0, sizeof ms);
+    std::vector<Range> ranges = {range(out, n * 4, true)};
+    for (uint32_t l = 0; l < K; ++l) {
+        if (!scales[l] || !nibbles[l])
+            return GCQ_ERR_NULL;
+        if (!aligned(scales[l], 4) || !aligned(nibbles[l], 4))
+            return GCQ_ERR_ALIGN;
+        ms.scales[l] = scales[l];
+        ms.nibbles[l] = nibbles[l];
+        ranges.push_back(range(scales[l], qsgd_num_buckets(n, d) * 4, false));
+        ranges.push_back(range(nibbles[l], qsgd_nibble_words(n) * 4, false));
+    }
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(
+        gcq::launch_qsgd_average(ms, K, n, d, s, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

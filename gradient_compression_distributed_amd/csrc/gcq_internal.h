@@ -35,6 +35,13 @@ struct DqWorkers {
     const uint32_t *w[GCQ_MAX_WORKERS];
 };
 
+// The K messages of qsgd_dequant_average (bucket scales and nibble words
+// per worker), passed by value in the kernel arguments.
+struct QsgdMsgs {
+    const float *scales[GCQ_MAX_WORKERS];
+    const uint32_t *nibbles[GCQ_MAX_WORKERS];
+};
+
 // Launch knobs (gcq_get_tuning / gcq_set_tuning).  They change the launch
 // shape only, never a result.
 gcq_tuning tuning();
@@ -64,8 +71,11 @@ hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint6
                         float eta, bool quant, hipStream_t stream);
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t,
                                  float *acc, hipStream_t stream);
+// maxnorm: bucket scale = largest magnitude (else the L2 norm).
 hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t s, uint64_t seed,
-                                float *norms, uint32_t *nibbles, hipStream_t stream);
+                                float *norms, uint32_t *nibbles, bool maxnorm, hipStream_t stream);
+hipError_t launch_qsgd_average(const QsgdMsgs &ms, uint32_t K, uint64_t n, uint32_t d, uint32_t s,
+                               float *out, hipStream_t stream);
 hipError_t launch_qsgd_dequant(const float *norms, const uint32_t *nibbles, uint64_t n, uint32_t d,
                                uint32_t s, float *out, hipStream_t stream);
 

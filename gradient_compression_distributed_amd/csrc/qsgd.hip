@@ -1,7 +1,8 @@
 // qsgd.hip -- QSGD bucketed s-level stochastic quantizer and its decode
 // ("QSGD: Communication-Efficient SGD via Gradient Quantization and
 // Encoding", chapterpal summary: Knowl 1 the Q_s operator, Knowl 2 the
-// (norm, sign, level) tuple, Knowl 3 decode, Knowl 8 bucketing) for gfx950.
+// (norm, sign, level) tuple, Knowl 3 decode and the K-worker average,
+// Knowl 8 bucketing and max-norm scaling) for gfx950.
 //
 // Per element: 4 B of gradient read, a 4-bit nibble (sign + 3-bit level)
 // and a 4/d-byte share of the bucket norm written; decode reads those and
@@ -165,6 +166,21 @@ __device__ __forceinline__ double wave_sum(double x)
     return x;
 }
 
+// Max-norm scaling (QSGD summary, Knowl 8): the running maximum of |g| that
+// a NaN never enters (compare, then select), and its wave reduction (the
+// maximum is exact, so the order does not matter).
+__device__ __forceinline__ float max_in(float m, float a) { return a > m ? a : m; }
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float y = __shfl_xor(x, off, kWave);
+        x = max_in(x, y);
+    }
+    return x;
+}
+
 // Fused norm + levels + nibbles for buckets of D = 256*C elements held in
 // registers: one wavefront per bucket, lane L holds elements 256c + 4L .. +3
 // (dwordx4 loads, 1 KiB per wave instruction).  The sum of squares is
@@ -174,7 +190,11 @@ __device__ __forceinline__ double wave_sum(double x)
 // pairs (2m, 2m+1) hold the two halves of word 32c + m of chunk c; one DPP
 // neighbour swap per two chunks lets even lanes store chunk c's words and
 // odd lanes chunk c+1's.
-template <int C, bool NT, bool Rcp>
+//
+// Max = true scales each bucket by its largest magnitude instead (Knowl 8).
+// A NaN does not enter that scale, so a bucket holding one takes the exact
+// level path (the division-free shortcut assumes finite inputs).
+template <int C, bool NT, bool Rcp, bool Max>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
     const float *__restrict__ g, uint32_t s, uint32_t k0, uint32_t k1, float *__restrict__ norms,
     uint32_t *__restrict__ nib, uint64_t nb_full)
@@ -196,19 +216,37 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c)
             uniforms4_int((base + 256u * c + 4u * lane) >> 2, k0, k1, U[c]);
-        double ss = 0.0;
+        float norm;
+        bool finite_bucket = true;
+        if constexpr (Max) {
+            float m = 0.0f;
+            bool nan = false;
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            ss = __builtin_fma((double)v[c].x, (double)v[c].x, ss);
-            ss = __builtin_fma((double)v[c].y, (double)v[c].y, ss);
-            ss = __builtin_fma((double)v[c].z, (double)v[c].z, ss);
-            ss = __builtin_fma((double)v[c].w, (double)v[c].w, ss);
+            for (int c = 0; c < C; ++c) {
+                m = max_in(m, fabsf(v[c].x));
+                m = max_in(m, fabsf(v[c].y));
+                m = max_in(m, fabsf(v[c].z));
+                m = max_in(m, fabsf(v[c].w));
+                nan = nan | (v[c].x != v[c].x) | (v[c].y != v[c].y) | (v[c].z != v[c].z) |
+                      (v[c].w != v[c].w);
+            }
+            norm = uniform_f(wave_max(m));
+            finite_bucket = !__any(nan);
+        } else {
+            double ss = 0.0;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                ss = __builtin_fma((double)v[c].x, (double)v[c].x, ss);
+                ss = __builtin_fma((double)v[c].y, (double)v[c].y, ss);
+                ss = __builtin_fma((double)v[c].z, (double)v[c].z, ss);
+                ss = __builtin_fma((double)v[c].w, (double)v[c].w, ss);
+            }
+            ss = wave_sum(ss);
+            norm = uniform_f((float)__builtin_sqrt(ss));
         }
-        ss = wave_sum(ss);
-        const float norm = uniform_f((float)__builtin_sqrt(ss));
         if (lane == 0)
             norms[b] = norm;
-        const bool fast = Rcp && rcp_norm_ok(norm);
+        const bool fast = Rcp && rcp_norm_ok(norm) && finite_bucket;
         const float rs = fast ? (1.0f / norm) * sf : 0.0f;
         uint32_t h[C];
 #pragma unroll
@@ -260,6 +298,8 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
 
 // Generic norms, any d: one thread per bucket (d <= 32, the bucket summed
 // in index order) or one wavefront per bucket (lanes stride the bucket).
+// (Max: the largest magnitude instead of the L2 norm.)
+template <bool Max>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_thread_kernel(
     const float *__restrict__ g, uint64_t n, uint32_t d, uint64_t b0, uint64_t nb,
     float *__restrict__ norms)
@@ -268,13 +308,21 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_thread_kernel(
     for (uint64_t b = b0 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
         const uint64_t lo = b * d;
         const uint64_t hi = lo + d < n ? lo + d : n;
-        double ss = 0.0;
-        for (uint64_t e = lo; e < hi; ++e)
-            ss = __builtin_fma((double)g[e], (double)g[e], ss);
-        norms[b] = (float)__builtin_sqrt(ss);
+        if constexpr (Max) {
+            float m = 0.0f;
+            for (uint64_t e = lo; e < hi; ++e)
+                m = max_in(m, fabsf(g[e]));
+            norms[b] = m;
+        } else {
+            double ss = 0.0;
+            for (uint64_t e = lo; e < hi; ++e)
+                ss = __builtin_fma((double)g[e], (double)g[e], ss);
+            norms[b] = (float)__builtin_sqrt(ss);
+        }
     }
 }
 
+template <bool Max>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_wave_kernel(
     const float *__restrict__ g, uint64_t n, uint32_t d, uint64_t b0, uint64_t nb,
     float *__restrict__ norms)
@@ -285,12 +333,21 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_wave_kernel(
          b += wstride) {
         const uint64_t lo = b * d;
         const uint64_t hi = lo + d < n ? lo + d : n;
-        double ss = 0.0;
-        for (uint64_t e = lo + lane; e < hi; e += kWave)
-            ss = __builtin_fma((double)g[e], (double)g[e], ss);
-        ss = wave_sum(ss);
-        if (lane == 0)
-            norms[b] = (float)__builtin_sqrt(ss);
+        if constexpr (Max) {
+            float m = 0.0f;
+            for (uint64_t e = lo + lane; e < hi; e += kWave)
+                m = max_in(m, fabsf(g[e]));
+            m = wave_max(m);
+            if (lane == 0)
+                norms[b] = m;
+        } else {
+            double ss = 0.0;
+            for (uint64_t e = lo + lane; e < hi; e += kWave)
+                ss = __builtin_fma((double)g[e], (double)g[e], ss);
+            ss = wave_sum(ss);
+            if (lane == 0)
+                norms[b] = (float)__builtin_sqrt(ss);
+        }
     }
 }
 
@@ -389,10 +446,154 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_kernel(
     }
 }
 
+// ---- K-worker decode-average (QSGD summary, Knowl 3) --------------------
+// out_i = (sum over workers l = 0..K-1, in order, from +0, of the decoded
+// value of worker l's nibble i) / K, each decoded value exactly
+// qsgd_dequant's +-((scale * level) / s).
+//
+// A workgroup owns a tile of 2048 elements (one nibble word per thread).
+// It first writes an LDS table: for worker l and each bucket the tile
+// touches, the 16 decoded values of the 16 possible nibbles (IEEE division,
+// once per entry).  Then each element and worker costs a nibble extract, a
+// table read and an add; no division per element.  Sums are staged through
+// LDS so every store instruction writes 1 KiB.
+constexpr uint64_t kAvgTileElems = 8u * kBlockThreads;
+
+template <bool Pow2K, bool NT>
+__global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms, uint32_t K,
+                                                                      uint64_t n, uint32_t d,
+                                                                      uint32_t s, uint32_t slots,
+                                                                      float kf, uint64_t ntiles,
+                                                                      float *__restrict__ out)
+{
+    extern __shared__ v4f avg_lds[];
+    float *table = (float *)avg_lds;                     // K * slots * 16 floats
+    v4f *stage = avg_lds + (size_t)K * slots * 4;        // 2048 floats
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const float sf = (float)s;
+    const uint64_t nwords = (n + 7) >> 3;
+    for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const uint64_t e_tile = tile * kAvgTileElems;
+        const uint64_t e_end = e_tile + kAvgTileElems < n ? e_tile + kAvgTileElems : n;
+        const uint64_t b0 = e_tile / d;
+        const uint32_t nbk = (uint32_t)((e_end - 1) / d - b0 + 1);   // <= slots
+        __syncthreads();   // the previous tile is done with the table and the stage
+        const uint32_t per_worker = nbk * 16u;
+        for (uint32_t i = tid; i < K * per_worker; i += kBlockThreads) {
+            const uint32_t l = i / per_worker;
+            const uint32_t rem = i - l * per_worker;
+            const uint32_t nib = rem & 15u;
+            float m = ms.scales[l][b0 + (rem >> 4)] * (float)(nib & 7u);
+            m = m / sf;
+            table[l * slots * 16u + rem] = (nib & 8u) ? -m : m;
+        }
+        __syncthreads();
+        const uint64_t wi = (e_tile >> 3) + tid;
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            a[e] = 0.0f;
+        if (wi < nwords) {
+            // bucket slot of each of the thread's 8 elements: at most one
+            // bucket boundary falls inside them (d >= 8 on this path).
+            // Elements past n may map to a slot that holds no table; their
+            // reads stay inside the allocation and they are never stored.
+            const uint32_t rel = (uint32_t)(wi * 8u - b0 * d);
+            const uint32_t bb0 = rel / d;
+            const uint32_t brk = (bb0 + 1u) * d - rel;
+            uint32_t off[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                off[e] = (bb0 + ((uint32_t)e >= brk ? 1u : 0u)) * 16u;
+            for (uint32_t l = 0; l < K; ++l) {
+                const uint32_t w = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l] + wi);
+                const float *tl = table + l * slots * 16u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    a[e] += tl[off[e] + ((w >> (28 - 4 * e)) & 15u)];
+            }
+        }
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            o[e] = Pow2K ? a[e] * kf : a[e] / kf;   // kf = 1/K (exact) or K
+        if (e_tile + kAvgTileElems <= n) {
+            v4f x0, x1;
+            x0.x = o[0]; x0.y = o[1]; x0.z = o[2]; x0.w = o[3];
+            x1.x = o[4]; x1.y = o[5]; x1.z = o[6]; x1.w = o[7];
+            stage[2 * tid] = x0;
+            stage[2 * tid + 1] = x1;
+            __syncthreads();
+            GCQ_GLOBAL v4f *o4 = (GCQ_GLOBAL v4f *)(out + e_tile + 512u * wave);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                st<NT>(o4 + 64 * q + lane, stage[128 * wave + 64 * q + lane]);
+        } else if (wi < nwords) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (wi * 8u + e < n)
+                    out[wi * 8u + e] = o[e];
+        }
+    }
+}
+
+// Any d and K: one thread per element, the division per worker as defined.
+template <bool Pow2K>
+__global__ __launch_bounds__(kBlockThreads) void qsgd_average_generic_kernel(
+    QsgdMsgs ms, uint32_t K, uint64_t n, uint32_t d, uint32_t s, float kf, float *__restrict__ out)
+{
+    const float sf = (float)s;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint64_t b = i / d;
+        const uint32_t sh = 28u - 4u * (uint32_t)(i & 7u);
+        float acc = 0.0f;
+        for (uint32_t l = 0; l < K; ++l) {
+            const uint32_t nib = (ms.nibbles[l][i >> 3] >> sh) & 15u;
+            float m = ms.scales[l][b] * (float)(nib & 7u);
+            m = m / sf;
+            acc += (nib & 8u) ? -m : m;
+        }
+        out[i] = Pow2K ? acc * kf : acc / kf;
+    }
+}
+
+template <int CC, bool Max>
+void launch_fused(const gcq_tuning &tu, uint32_t grid, const float *g, uint32_t s, uint32_t k0,
+                  uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
+                  hipStream_t stream)
+{
+    if (tu.qsgd_nt && tu.qsgd_rcp)
+        qsgd_fused_kernel<CC, true, true, Max>
+            <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
+    else if (tu.qsgd_nt)
+        qsgd_fused_kernel<CC, true, false, Max>
+            <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
+    else if (tu.qsgd_rcp)
+        qsgd_fused_kernel<CC, false, true, Max>
+            <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
+    else
+        qsgd_fused_kernel<CC, false, false, Max>
+            <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
+}
+
+template <bool Max>
+void launch_fused_c(uint32_t C, const gcq_tuning &tu, uint32_t grid, const float *g, uint32_t s,
+                    uint32_t k0, uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
+                    hipStream_t stream)
+{
+    switch (C) {
+    case 1: launch_fused<1, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
+    case 2: launch_fused<2, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
+    case 4: launch_fused<4, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
+    default: launch_fused<8, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t s, uint64_t seed,
-                                float *norms, uint32_t *nibbles, hipStream_t stream)
+                                float *norms, uint32_t *nibbles, bool maxnorm, hipStream_t stream)
 {
     if (!n)
         return hipSuccess;
@@ -407,26 +608,10 @@ hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t
         if (nb_done) {
             const uint32_t grid =
                 grid_for((nb_done + kBlockWaves - 1) / kBlockWaves, tu.qsgd_blocks_per_cu);
-#define GCQ_FUSED(CC)                                                                  \
-    if (tu.qsgd_nt && tu.qsgd_rcp)                                                     \
-        qsgd_fused_kernel<CC, true, true><<<grid, kBlockThreads, 0, stream>>>(         \
-            g, s, k0, k1, norms, nibbles, nb_done);                                    \
-    else if (tu.qsgd_nt)                                                               \
-        qsgd_fused_kernel<CC, true, false><<<grid, kBlockThreads, 0, stream>>>(        \
-            g, s, k0, k1, norms, nibbles, nb_done);                                    \
-    else if (tu.qsgd_rcp)                                                              \
-        qsgd_fused_kernel<CC, false, true><<<grid, kBlockThreads, 0, stream>>>(        \
-            g, s, k0, k1, norms, nibbles, nb_done);                                    \
-    else                                                                               \
-        qsgd_fused_kernel<CC, false, false><<<grid, kBlockThreads, 0, stream>>>(       \
-            g, s, k0, k1, norms, nibbles, nb_done);
-            switch (C) {
-            case 1: GCQ_FUSED(1) break;
-            case 2: GCQ_FUSED(2) break;
-            case 4: GCQ_FUSED(4) break;
-            default: GCQ_FUSED(8) break;
-            }
-#undef GCQ_FUSED
+if (maxnorm)
+                launch_fused_c<true>(C, tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream);
+            else
+                launch_fused_c<false>(C, tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
@@ -436,12 +621,20 @@ hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t
         const uint64_t left = nb - nb_done;
         if (d <= 32) {
             const uint32_t grid = grid_for((left + kBlockThreads - 1) / kBlockThreads, 0);
-            qsgd_norms_thread_kernel<<<grid, kBlockThreads, 0, stream>>>(g, n, d, nb_done, nb,
-                                                                         norms);
+            if (maxnorm)
+                qsgd_norms_thread_kernel<true>
+                    <<<grid, kBlockThreads, 0, stream>>>(g, n, d, nb_done, nb, norms);
+            else
+                qsgd_norms_thread_kernel<false>
+                    <<<grid, kBlockThreads, 0, stream>>>(g, n, d, nb_done, nb, norms);
         } else {
             const uint32_t grid = grid_for((left + kBlockWaves - 1) / kBlockWaves, 0);
-            qsgd_norms_wave_kernel<<<grid, kBlockThreads, 0, stream>>>(g, n, d, nb_done, nb,
-                                                                       norms);
+            if (maxnorm)
+                qsgd_norms_wave_kernel<true>
+                    <<<grid, kBlockThreads, 0, stream>>>(g, n, d, nb_done, nb, norms);
+            else
+                qsgd_norms_wave_kernel<false>
+                    <<<grid, kBlockThreads, 0, stream>>>(g, n, d, nb_done, nb, norms);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -484,6 +677,47 @@ hipError_t launch_qsgd_dequant(const float *norms, const uint32_t *nibbles, uint
             GCQ_DQ(false, false);
     }
 #undef GCQ_DQ
+    return hipGetLastError();
+}
+
+hipError_t launch_qsgd_average(const QsgdMsgs &ms, uint32_t K, uint64_t n, uint32_t d, uint32_t s,
+                               float *out, hipStream_t stream)
+{
+    if (!n)
+        return hipSuccess;
+    const gcq_tuning tu = tuning();
+    const bool pow2 = (K & (K - 1u)) == 0u;
+    const float kf = pow2 ? 1.0f / (float)K : (float)K;   // 1/K is exact for K = 2^j
+    // buckets a 2048-element tile can touch
+    const uint64_t slots = (kAvgTileElems - 1) / d + 2;
+    const uint64_t lds = ((uint64_t)K * slots * 16u + kAvgTileElems) * 4u;
+    if (d >= 256u && d <= (1u << 30) && lds <= 64u * 1024u) {
+        const uint64_t ntiles = (n + kAvgTileElems - 1) / kAvgTileElems;
+        const uint32_t grid = grid_for(ntiles, tu.qsgd_dequant_blocks_per_cu);
+#define GCQ_AVG(P, NT)                                                                        \
+    qsgd_average_kernel<P, NT><<<grid, kBlockThreads, (size_t)lds, stream>>>(                 \
+        ms, K, n, d, s, (uint32_t)slots, kf, ntiles, out)
+        if (pow2) {
+            if (tu.qsgd_dequant_nt)
+                GCQ_AVG(true, true);
+            else
+                GCQ_AVG(true, false);
+        } else {
+            if (tu.qsgd_dequant_nt)
+                GCQ_AVG(false, true);
+            else
+                GCQ_AVG(false, false);
+        }
+#undef GCQ_AVG
+    } else {
+        const uint32_t grid = grid_for((n + kBlockThreads - 1) / kBlockThreads, 0);
+        if (pow2)
+            qsgd_average_generic_kernel<true>
+                <<<grid, kBlockThreads, 0, stream>>>(ms, K, n, d, s, kf, out);
+        else
+            qsgd_average_generic_kernel<false>
+                <<<grid, kBlockThreads, 0, stream>>>(ms, K, n, d, s, kf, out);
+    }
     return hipGetLastError();
 }
 

@@ -14,8 +14,8 @@
  *     compression read the same gradient buffer).
  *   - "QSGD: Communication-Efficient SGD via Gradient Quantization and
  *     Encoding" (chapterpal summary): Knowl 1 (Q_s), Knowl 2 (the
- *     (norm, sign, level) tuple), Knowl 3 (encode, broadcast, decode),
- *     Knowl 8 (bucketing).
+ *     (norm, sign, level) tuple), Knowl 3 (encode, broadcast, decode,
+ *     average), Knowl 8 (bucketing, max-norm scaling).
  *   - blog "IMerge修改（Design）": consecutive layers merged into
  *     transmission units (fusion buckets), one unit per message.
  *
@@ -244,6 +244,43 @@ int qsgd_quantize(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t see
  */
 int qsgd_dequant(const float *norms, const uint32_t *nibbles, size_t n, uint32_t d,
                  uint32_t s, float *out, void *stream);
+
+/*
+ * qsgd_quantize_maxnorm -- qsgd_quantize with the max-norm bucket scale of
+ * the QSGD summary's Knowl 8: each bucket is normalized by its largest
+ * coordinate magnitude instead of its L2 norm.  scales[b] = max |g_i| over
+ * bucket b (exact; a NaN element never becomes the scale and quantizes to
+ * level 0; an all-zero bucket has scale +0 and levels 0).  Levels, signs,
+ * nibbles, uniforms and arguments exactly as qsgd_quantize, with scales in
+ * place of norms; qsgd_dequant decodes the result.
+ *
+ * Errors: as qsgd_quantize.
+ */
+int qsgd_quantize_maxnorm(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed,
+                          float *scales, uint32_t *nibbles, void *stream);
+
+/*
+ * qsgd_dequant_average -- the receiving side of the QSGD summary's Knowl 3:
+ * decode the messages of all K workers and average them,
+ *     out[i] = ( sum over l = 0..K-1, in this order, starting from +0,
+ *                of +-((scales[l][i/d] * level_l,i) / s) ) / K
+ * in float32, each decoded value exactly as qsgd_dequant computes it, and
+ * the sum divided by K once (correctly rounded).  Works with L2 norms or
+ * max-norm scales.
+ *
+ *   scales   host array of K device pointers, float32[ceil(n/d)] each,
+ *            4-byte aligned
+ *   nibbles  host array of K device pointers, uint32[ceil(n/8)] each,
+ *            4-byte aligned
+ *   K        1..GCQ_MAX_WORKERS
+ *   n, d, s  as qsgd_dequant
+ *   out      out, float32[n], 16-byte aligned
+ *
+ * Errors: GCQ_ERR_PARAM (K, d or s), GCQ_ERR_NULL, GCQ_ERR_ALIGN,
+ * GCQ_ERR_OVERLAP (out intersects an input), GCQ_ERR_LAUNCH.
+ */
+int qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibbles, uint32_t K,
+                         size_t n, uint32_t d, uint32_t s, float *out, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Sizes and status names (pure host functions, no device access)      */

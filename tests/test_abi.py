@@ -171,6 +171,32 @@ def test_qsgd_validation(lib):
     assert dq(nm, nb, n, 512, 7, nb) == E_OVERLAP
 
 
+def test_qsgd_maxnorm_and_average_validation(lib):
+    n = 1000
+    g, nm, nb, out = A, A + (1 << 20), A + (2 << 20), A + (3 << 20)
+    q = lambda g_, d, s: lib.qsgd_quantize_maxnorm(vp(g_), n, d, s, ctypes.c_uint64(1), vp(nm),
+                                                   vp(nb), NULL)
+    assert q(g, 0, 7) == E_PARAM
+    assert q(g, 512, 8) == E_PARAM
+    assert q(0, 512, 7) == E_NULL
+    assert q(g + 4, 512, 7) == E_ALIGN
+    arr = lambda xs: (ctypes.c_void_p * len(xs))(*[vp(x) for x in xs])
+    sc = [A + (4 << 20) + k * (1 << 16) for k in range(3)]
+    nbs = [A + (5 << 20) + k * (1 << 16) for k in range(3)]
+    av = lambda s_, n_, K, d, s, o: lib.qsgd_dequant_average(s_, n_, K, n, d, s, vp(o), NULL)
+    assert av(arr(sc), arr(nbs), 0, 512, 7, out) == E_PARAM
+    assert av(arr(sc), arr(nbs), 65, 512, 7, out) == E_PARAM
+    assert av(arr(sc), arr(nbs), 3, 0, 7, out) == E_PARAM
+    assert av(arr(sc), arr(nbs), 3, 512, 0, out) == E_PARAM
+    assert av(None, arr(nbs), 3, 512, 7, out) == E_NULL
+    assert av(arr(sc), arr(nbs), 3, 512, 7, 0) == E_NULL
+    assert av(arr([sc[0], 0, sc[2]]), arr(nbs), 3, 512, 7, out) == E_NULL
+    assert av(arr(sc), arr(nbs), 3, 512, 7, out + 4) == E_ALIGN
+    assert av(arr([sc[0] + 2, sc[1], sc[2]]), arr(nbs), 3, 512, 7, out) == E_ALIGN
+    assert av(arr(sc), arr(nbs), 3, 512, 7, nbs[1] - 16) == E_OVERLAP
+    assert lib.qsgd_dequant_average(arr(sc), arr(nbs), 3, 0, 512, 7, vp(out), NULL) == OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     g = torch.zeros(16)
