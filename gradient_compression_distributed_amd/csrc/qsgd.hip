@@ -458,17 +458,50 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_kernel(
 // table read and an add; no division per element.  Sums are staged through
 // LDS so every store instruction writes 1 KiB.
 constexpr uint64_t kAvgTileElems = 8u * kBlockThreads;
+constexpr uint32_t kAvgChunk = 8;   // worker words loaded before they are decoded
+// table rows per worker: the buckets a 2048-element tile can touch when
+// d >= 228 (2047/d + 2 <= 10); smaller buckets take the per-element kernel
+constexpr uint32_t kAvgSlots = 10;
+constexpr uint32_t kAvgWorkerBytes = kAvgSlots * 64u;
+
+// Add one worker's nibble word (8 elements) into the running sums: the
+// nibbles, times 4 (a byte offset into a 16-float table row), are spread
+// one per byte -- elements 0, 2, 4, 6 in `hi`, 1, 3, 5, 7 in `lo`, first
+// element in the top byte -- so each element's table address is its row
+// (off, which already holds the chunk's worker base) plus one byte of a
+// register, and the worker's place in the chunk is the LDS instruction's
+// immediate offset.  The empty asm keeps the compiler from folding the
+// byte extraction back into a shift-and-mask per element.  All eight table
+// reads are issued before the additions.
+template <uint32_t J>
+__device__ __forceinline__ void avg_word(float (&a)[8], uint32_t w, const char *tb,
+                                         const uint32_t (&off)[8])
+{
+    uint32_t hi = (w >> 2) & 0x3C3C3C3Cu;
+    uint32_t lo = (w << 2) & 0x3C3C3C3Cu;
+    asm volatile("" : "+v"(hi), "+v"(lo));
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t src = (e & 1) ? lo : hi;
+        const uint32_t byte = (src >> (8 * (3 - e / 2))) & 0xFFu;
+        t[e] = *(const float *)(tb + (off[e] + byte) + J * kAvgWorkerBytes);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        a[e] += t[e];
+}
 
 template <bool Pow2K, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms, uint32_t K,
                                                                       uint64_t n, uint32_t d,
-                                                                      uint32_t s, uint32_t slots,
+                                                                      uint32_t s,
                                                                       float kf, uint64_t ntiles,
                                                                       float *__restrict__ out)
 {
     extern __shared__ v4f avg_lds[];
-    float *table = (float *)avg_lds;                     // K * slots * 16 floats
-    v4f *stage = avg_lds + (size_t)K * slots * 4;        // 2048 floats
+    float *table = (float *)avg_lds;                     // K * kAvgSlots * 16 floats
+    v4f *stage = avg_lds + (size_t)K * kAvgSlots * 4;    // 2048 floats
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const float sf = (float)s;
     const uint64_t nwords = (n + 7) >> 3;
@@ -476,24 +509,47 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
         const uint64_t e_tile = tile * kAvgTileElems;
         const uint64_t e_end = e_tile + kAvgTileElems < n ? e_tile + kAvgTileElems : n;
         const uint64_t b0 = e_tile / d;
-        const uint32_t nbk = (uint32_t)((e_end - 1) / d - b0 + 1);   // <= slots
+        const uint32_t nbk = (uint32_t)((e_end - 1) / d - b0 + 1);   // <= kAvgSlots
         __syncthreads();   // the previous tile is done with the table and the stage
-        const uint32_t per_worker = nbk * 16u;
-        for (uint32_t i = tid; i < K * per_worker; i += kBlockThreads) {
-            const uint32_t l = i / per_worker;
-            const uint32_t rem = i - l * per_worker;
-            const uint32_t nib = rem & 15u;
-            float m = ms.scales[l][b0 + (rem >> 4)] * (float)(nib & 7u);
-            m = m / sf;
-            table[l * slots * 16u + rem] = (nib & 8u) ? -m : m;
+        const uint64_t wi = (e_tile >> 3) + tid;
+        const bool valid = wi < nwords;
+        // the first chunk's nibble words do not depend on the table: their
+        // loads are issued before it is built
+        uint32_t w[kAvgChunk];
+        if (valid && K >= kAvgChunk) {
+#pragma unroll
+            for (uint32_t j = 0; j < kAvgChunk; ++j)
+                w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
+        }
+        // thread (l, nib) = (tid / 16 + 16 j, tid % 16) fills nibble nib of
+        // worker l for every bucket of the tile; its scale loads are issued
+        // together
+        {
+            const uint32_t nib = tid & 15u;
+            const float lev = (float)(nib & 7u);
+            for (uint32_t l = tid >> 4; l < K; l += kBlockThreads / 16u) {
+                const GCQ_GLOBAL float *sc = (const GCQ_GLOBAL float *)ms.scales[l] + b0;
+                float v[kAvgSlots];
+#pragma unroll
+                for (uint32_t bb = 0; bb < kAvgSlots; ++bb)
+                    v[bb] = bb < nbk ? sc[bb] : 0.0f;
+                float *tl = table + l * (kAvgWorkerBytes / 4u) + nib;
+#pragma unroll
+                for (uint32_t bb = 0; bb < kAvgSlots; ++bb) {
+                    if (bb < nbk) {
+                        float m = v[bb] * lev;
+                        m = m / sf;
+                        tl[16u * bb] = (nib & 8u) ? -m : m;
+                    }
+                }
+            }
         }
         __syncthreads();
-        const uint64_t wi = (e_tile >> 3) + tid;
         float a[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             a[e] = 0.0f;
-        if (wi < nwords) {
+        if (valid) {
             // bucket slot of each of the thread's 8 elements: at most one
             // bucket boundary falls inside them (d >= 8 on this path).
             // Elements past n may map to a slot that holds no table; their
@@ -501,16 +557,40 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
             const uint32_t rel = (uint32_t)(wi * 8u - b0 * d);
             const uint32_t bb0 = rel / d;
             const uint32_t brk = (bb0 + 1u) * d - rel;
-            uint32_t off[8];
+            uint32_t off[8];   // byte offset of each element's table row
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                off[e] = (bb0 + ((uint32_t)e >= brk ? 1u : 0u)) * 16u;
-            for (uint32_t l = 0; l < K; ++l) {
-                const uint32_t w = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l] + wi);
-                const float *tl = table + l * slots * 16u;
+                off[e] = (bb0 + ((uint32_t)e >= brk ? 1u : 0u)) * 64u;
+            const char *tb = (const char *)table;
+            uint32_t l = 0;
+            // groups of kAvgChunk workers: every load issued, then decoded
+            for (; l + kAvgChunk <= K; l += kAvgChunk) {
+                if (l) {
+#pragma unroll
+                    for (uint32_t j = 0; j < kAvgChunk; ++j)
+                        w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l + j] + wi);
+                }
+                uint32_t offc[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    offc[e] = off[e] + l * kAvgWorkerBytes;
+                    asm volatile("" : "+v"(offc[e]));   // one add per chunk, not per read
+                }
+                avg_word<0>(a, w[0], tb, offc);
+                avg_word<1>(a, w[1], tb, offc);
+                avg_word<2>(a, w[2], tb, offc);
+                avg_word<3>(a, w[3], tb, offc);
+                avg_word<4>(a, w[4], tb, offc);
+                avg_word<5>(a, w[5], tb, offc);
+                avg_word<6>(a, w[6], tb, offc);
+                avg_word<7>(a, w[7], tb, offc);
+            }
+            for (; l < K; ++l) {
+                uint32_t offc[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    a[e] += tl[off[e] + ((w >> (28 - 4 * e)) & 15u)];
+                    offc[e] = off[e] + l * kAvgWorkerBytes;
+                avg_word<0>(a, ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l] + wi), tb, offc);
             }
         }
         float o[8];
@@ -690,13 +770,13 @@ hipError_t launch_qsgd_average(const QsgdMsgs &ms, uint32_t K, uint64_t n, uint3
     const float kf = pow2 ? 1.0f / (float)K : (float)K;   // 1/K is exact for K = 2^j
     // buckets a 2048-element tile can touch
     const uint64_t slots = (kAvgTileElems - 1) / d + 2;
-    const uint64_t lds = ((uint64_t)K * slots * 16u + kAvgTileElems) * 4u;
-    if (d >= 256u && d <= (1u << 30) && lds <= 64u * 1024u) {
+    const uint64_t lds = ((uint64_t)K * kAvgSlots * 16u + kAvgTileElems) * 4u;
+    if (slots <= kAvgSlots && d <= (1u << 30) && lds <= 64u * 1024u) {
         const uint64_t ntiles = (n + kAvgTileElems - 1) / kAvgTileElems;
         const uint32_t grid = grid_for(ntiles, tu.qsgd_dequant_blocks_per_cu);
 #define GCQ_AVG(P, NT)                                                                        \
     qsgd_average_kernel<P, NT><<<grid, kBlockThreads, (size_t)lds, stream>>>(                 \
-        ms, K, n, d, s, (uint32_t)slots, kf, ntiles, out)
+        ms, K, n, d, s, kf, ntiles, out)
         if (pow2) {
             if (tu.qsgd_dequant_nt)
                 GCQ_AVG(true, true);
