@@ -22,6 +22,10 @@ passage of the pages it follows:
 * ``qsgd_maxnorms`` / ``qsgd_quantize_maxnorm`` -- Knowl 8, max-norm
   scaling; ``qsgd_dequant_average`` -- Knowl 3 (decode every peer's message
   and average).
+* ``saps_keep`` / ``saps_gather`` / ``saps_merge`` -- SAPS ("Communication-
+  Efficient Decentralized Learning with Sparsification and Adaptive Peer
+  Selection"): the shared-seed Bernoulli(1/c) mask and the single-peer
+  exchange.
 * ``philox4x32_10`` / ``uniform`` -- the SC'11 Philox-4x32 generator.  The
   pages name no random source, so the exact uniform stream is
   "parity unpinned" by the pages; it is pinned only statistically.
@@ -69,6 +73,12 @@ def _load():
     lib.oracle_qsgd_quantize.argtypes = [vp, sz, u32, u32, u64, vp, vp]
     lib.oracle_qsgd_quantize.restype = None
     lib.oracle_qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp]
+    lib.oracle_saps_keep.argtypes = [u64, u64, f32]
+    lib.oracle_saps_keep.restype = ctypes.c_int
+    lib.oracle_saps_gather.argtypes = [vp, sz, f32, u64, vp]
+    lib.oracle_saps_gather.restype = sz
+    lib.oracle_saps_merge.argtypes = [vp, sz, f32, u64, vp]
+    lib.oracle_saps_merge.restype = sz
     lib.oracle_qsgd_maxnorms.argtypes = [vp, sz, u32, vp]
     lib.oracle_qsgd_maxnorms.restype = None
     lib.oracle_qsgd_quantize_maxnorm.argtypes = [vp, sz, u32, u32, u64, vp, vp]
@@ -266,3 +276,25 @@ def qsgd_dequant_average(scales: list, nibbles: list, n: int, d: int, s: int) ->
     out = np.empty(n, dtype=np.float32)
     lib.oracle_qsgd_dequant_average(sp, npp, K, n, d, s, _ptr(out))
     return out
+
+
+def saps_keep(seed: int, n: int, c: float) -> np.ndarray:
+    """The mask: keep[i] for i < n (a bool array; one oracle call each)."""
+    lib = _load()
+    return np.array([bool(lib.oracle_saps_keep(seed, i, ctypes.c_float(c))) for i in range(n)])
+
+
+def saps_gather(x: np.ndarray, c: float, seed: int) -> np.ndarray:
+    lib = _load()
+    _f32(x, "x")
+    vals = np.empty(x.size, dtype=np.float32)
+    k = lib.oracle_saps_gather(_ptr(x), x.size, ctypes.c_float(c), ctypes.c_uint64(seed), _ptr(vals))
+    return vals[:k].copy()
+
+
+def saps_merge(x: np.ndarray, c: float, seed: int, peer: np.ndarray) -> int:
+    """x[kept] = (x[kept] + peer) * 0.5 in place; returns the count used."""
+    lib = _load()
+    _f32(x, "x"), _f32(peer, "peer")
+    return int(lib.oracle_saps_merge(_ptr(x), x.size, ctypes.c_float(c), ctypes.c_uint64(seed),
+                                     _ptr(peer)))

@@ -24,6 +24,9 @@
  *         Encoding" (chapterpal summary): Knowl 1 (the Q_s operator),
  *         Knowl 2 (the (norm, sign, level) tuple), Knowl 3 (decode and
  *         average), Knowl 8 (bucketing, max-norm scaling).
+ *   [SA]  "Communication-Efficient Decentralized Learning with Sparsification
+ *         and Adaptive Peer Selection": the shared-seed Bernoulli(1/c)
+ *         sparsification mask and the single-peer gossip exchange.
  *   [PH]  Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *         1, 2, 3" (SC'11): the Philox-4x32 counter-based generator.  The
  *         pages name no random source; this generator is a frozen choice,
@@ -356,4 +359,53 @@ void oracle_qsgd_dequant_average(const float *const *scales, const uint32_t *con
         }
         out[i] = acc / kf;
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* SAPS: shared-seed random sparsification and single-peer exchange    */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [SA] The model is sparsified by a mask whose entries follow a Bernoulli
+ * distribution with probability 1/c, generated from a seed that the
+ * coordinator hands every worker, so all workers mask the same components
+ * and only the components at mask positions travel (the receiver knows the
+ * positions from the seed).  Reading taken: element i is kept when
+ * u_i * c < 1, evaluated exactly (u_i is oracle_uniform(seed, i), a 24-bit
+ * fraction; the product of it and a float fits a double exactly).
+ */
+int oracle_saps_keep(uint64_t seed, uint64_t i, float c)
+{
+    double u = (double)oracle_uniform(seed, i);
+    return u * (double)(c * 1.0001f) < 1.0;
+}
+
+/* The kept components of x, in index order; returns how many. */
+size_t oracle_saps_gather(const float *x, size_t n, float c, uint64_t seed, float *values)
+{
+    size_t k = 0;
+    for (size_t i = 0; i < n; i++)
+        if (oracle_saps_keep(seed, i, c))
+            values[k++] = x[i];
+    return k;
+}
+
+/*
+ * [SA] single-peer gossip: each row of the gossip matrix has two non-zero
+ * entries and the matrix is doubly stochastic.  Reading taken: an exchanged
+ * component becomes the average of the two workers' values, (x + y) * 0.5
+ * in float32 (the sum rounded, the halving exact); components outside the
+ * mask are left as they are.  peer holds the peer's kept values in index
+ * order; returns how many were used.
+ */
+size_t oracle_saps_merge(float *x, size_t n, float c, uint64_t seed, const float *peer)
+{
+    size_t k = 0;
+    for (size_t i = 0; i < n; i++) {
+        if (oracle_saps_keep(seed, i, c)) {
+            x[i] = (x[i] + peer[k]) * 0.5f;
+            k++;
+        }
+    }
+    return k;
 }
