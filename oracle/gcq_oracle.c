@@ -377,7 +377,7 @@ void oracle_qsgd_dequant_average(const float *const *scales, const uint32_t *con
 int oracle_saps_keep(uint64_t seed, uint64_t i, float c)
 {
     double u = (double)oracle_uniform(seed, i);
-    return u * (double)(c * 1.0001f) < 1.0;
+    return u * (double)c < 1.0;
 }
 
 /* The kept components of x, in index order; returns how many. */
