@@ -246,6 +246,27 @@ def main():
                               "bytes_per_element": round(bpe, 4)}
         next_ops["qsgd_dequant_average"]["config"] = {"K": K, "d": QSGD_D, "s": QSGD_S, "n": n}
 
+        # SAPS shared-seed sparsification at c = 100 (99% of the components
+        # dropped): mask (+ offsets), gather of the kept components, merge of a
+        # peer's; algorithmic bytes count the mask bits and the kept elements
+        c_saps, seed_saps = 100.0, wl.qsgd_seed(9)
+        smask = torch.empty(gcq.saps_mask_words(n), dtype=torch.int32, device=dev)
+        soffs = torch.empty(gcq.saps_num_tiles(n) + 1, dtype=torch.int64, device=dev)
+        mask_ms = timed(lambda: gcq.saps_mask(n, c_saps, seed_saps, mask=smask, offsets=soffs))
+        kept = gcq.saps_count(soffs)
+        svals = torch.empty(kept, dtype=torch.float32, device=dev)
+        gat_ms = timed(lambda: gcq.saps_gather(g, smask, soffs, values=svals))
+        mer_ms = timed(lambda: gcq.saps_merge(wloc, smask, soffs, svals))
+        kf = kept / n
+        for name, ms, bpe in (("saps_mask", mask_ms, 0.125),
+                              ("saps_gather", gat_ms, 0.125 + 8.0 * kf),
+                              ("saps_merge", mer_ms, 0.125 + 12.0 * kf)):
+            gbps = bpe * n / (ms / 1e3) / 1e9
+            next_ops[name] = {"ms": round(ms, 4), "elements_per_s": n / (ms / 1e3),
+                              "GBps": round(gbps, 1), "bytes_per_element": round(bpe, 4)}
+        next_ops["saps_mask"]["config"] = {"c": c_saps, "n": n, "kept": kept}
+        del smask, soffs, svals
+
     copy_gbps = None
     if args.copy_calibration:
         src = grads[0]

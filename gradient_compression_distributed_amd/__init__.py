@@ -21,6 +21,7 @@ __all__ = [
     "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "get_tuning", "BucketList",
     "cdsgd_update_quantize", "cdsgd_local_update", "cdsgd_compresses",
     "qsgd_quantize_maxnorm", "qsgd_dequant_average",
+    "saps_mask", "saps_gather", "saps_merge", "saps_mask_words", "saps_num_tiles",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +87,16 @@ def load():
     lib.qsgd_dequant_average.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), u32, sz, u32,
                                          u32, vp, vp]
     lib.qsgd_dequant_average.restype = i32
+    lib.saps_mask.argtypes = [sz, f32, u64, vp, vp, vp]
+    lib.saps_mask.restype = i32
+    lib.saps_gather.argtypes = [vp, sz, vp, vp, vp, sz, vp]
+    lib.saps_gather.restype = i32
+    lib.saps_merge.argtypes = [vp, sz, vp, vp, vp, sz, vp]
+    lib.saps_merge.restype = i32
+    lib.saps_mask_words.argtypes = [sz]
+    lib.saps_mask_words.restype = sz
+    lib.saps_num_tiles.argtypes = [sz]
+    lib.saps_num_tiles.restype = sz
     lib.cdsgd_local_update.argtypes = [vp, vp, sz, f32, vp]
     lib.cdsgd_local_update.restype = i32
     lib.gc2_packed_words.argtypes = [sz]
@@ -336,3 +347,63 @@ def qsgd_dequant(norms, nibbles, n: int, d: int, s: int, out=None):
     _check(lib.qsgd_dequant(_ptr(norms), _ptr(nibbles), n, d, s, _ptr(out),
                             _stream(out.device)), "qsgd_dequant")
     return out
+
+
+# ------------------------------------------------------------------ SAPS
+def saps_mask_words(n: int) -> int:
+    return int(load().saps_mask_words(n))
+
+
+def saps_num_tiles(n: int) -> int:
+    return int(load().saps_num_tiles(n))
+
+
+def saps_mask(n: int, c: float, seed: int, mask=None, offsets=None, device="cuda"):
+    """Shared-seed Bernoulli(1/c) mask: returns (mask words int32, tile
+    offsets int64 with the total kept count last)."""
+    import torch
+
+    lib = load()
+    if mask is None:
+        mask = torch.empty(saps_mask_words(n), dtype=torch.int32, device=device)
+    if offsets is None:
+        offsets = torch.empty(saps_num_tiles(n) + 1, dtype=torch.int64, device=device)
+    _dev(mask, torch.int32, "mask", saps_mask_words(n))
+    _dev(offsets, torch.int64, "offsets", saps_num_tiles(n) + 1)
+    _check(lib.saps_mask(n, ctypes.c_float(c), ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+                         _ptr(mask), _ptr(offsets), _stream(offsets.device)), "saps_mask")
+    return mask, offsets
+
+
+def saps_count(offsets) -> int:
+    """The total kept count (synchronizes with the device)."""
+    return int(offsets[-1].item())
+
+
+def saps_gather(x, mask, offsets, values=None):
+    """The kept components of ``x`` in index order."""
+    import torch
+
+    lib = load()
+    _dev(x, torch.float32, "x")
+    _dev(mask, torch.int32, "mask", saps_mask_words(x.numel()))
+    _dev(offsets, torch.int64, "offsets", saps_num_tiles(x.numel()) + 1)
+    if values is None:
+        values = torch.empty(saps_count(offsets), dtype=torch.float32, device=x.device)
+    _dev(values, torch.float32, "values")
+    _check(lib.saps_gather(_ptr(x), x.numel(), _ptr(mask), _ptr(offsets), _ptr(values),
+                           values.numel(), _stream(x.device)), "saps_gather")
+    return values
+
+
+def saps_merge(x, mask, offsets, peer_values):
+    """x[kept] = (x[kept] + peer_values) * 0.5, in place."""
+    import torch
+
+    lib = load()
+    _dev(x, torch.float32, "x")
+    _dev(mask, torch.int32, "mask", saps_mask_words(x.numel()))
+    _dev(offsets, torch.int64, "offsets", saps_num_tiles(x.numel()) + 1)
+    _dev(peer_values, torch.float32, "peer_values")
+    _check(lib.saps_merge(_ptr(x), x.numel(), _ptr(mask), _ptr(offsets), _ptr(peer_values),
+                          peer_values.numel(), _stream(x.device)), "saps_merge")

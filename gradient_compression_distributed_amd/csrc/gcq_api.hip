@@ -430,4 +430,60 @@ int qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibb
         gcq::launch_qsgd_average(ms, K, n, d, s, out, (hipStream_t)stream));
 }
 
+size_t saps_mask_words(size_t n) { return n / 32 + (n % 32 != 0); }
+
+size_t saps_num_tiles(size_t n) { return n / 8192 + (n % 8192 != 0); }
+
+int saps_mask(size_t n, float c, uint64_t seed, uint32_t *mask_words, uint64_t *tile_offsets,
+              void *stream)
+{
+    if (!(isfinite(c) && c >= 1.0f) || n > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (!tile_offsets || (n && !mask_words))
+        return GCQ_ERR_NULL;
+    if (!aligned(mask_words, 4) || !aligned(tile_offsets, 8))
+        return GCQ_ERR_ALIGN;
+    std::vector<Range> ranges = {range(mask_words, saps_mask_words(n) * 4, true),
+                                 range(tile_offsets, (saps_num_tiles(n) + 1) * 8, true)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(
+        gcq::launch_saps_mask(n, c, seed, mask_words, tile_offsets, (hipStream_t)stream));
+}
+
+static int saps_apply(float *x, size_t n, const uint32_t *mask_words, const uint64_t *tile_offsets,
+                      float *values, size_t capacity, bool merge, void *stream)
+{
+    if (n > kMaxElems || capacity > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!x || !mask_words || !tile_offsets || (capacity && !values))
+        return GCQ_ERR_NULL;
+    if (!aligned(x, 4) || !aligned(mask_words, 4) || !aligned(tile_offsets, 8) ||
+        !aligned(values, 4))
+        return GCQ_ERR_ALIGN;
+    std::vector<Range> ranges = {range(x, n * 4, merge),
+                                 range(mask_words, saps_mask_words(n) * 4, false),
+                                 range(tile_offsets, (saps_num_tiles(n) + 1) * 8, false),
+                                 range(values, capacity * 4, !merge)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(gcq::launch_saps_apply(x, n, mask_words, tile_offsets, values, capacity,
+                                                merge, (hipStream_t)stream));
+}
+
+int saps_gather(const float *x, size_t n, const uint32_t *mask_words,
+                const uint64_t *tile_offsets, float *values, size_t capacity, void *stream)
+{
+    return saps_apply((float *)x, n, mask_words, tile_offsets, values, capacity, false, stream);
+}
+
+int saps_merge(float *x, size_t n, const uint32_t *mask_words, const uint64_t *tile_offsets,
+               const float *peer_values, size_t capacity, void *stream)
+{
+    return saps_apply(x, n, mask_words, tile_offsets, (float *)peer_values, capacity, true,
+                      stream);
+}
+
 }  // extern "C"

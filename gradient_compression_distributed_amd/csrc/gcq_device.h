@@ -1,6 +1,6 @@
 // gcq_device.h -- device-side helpers shared by the kernels: 16-byte vector
 // type, global-address-space qualifier, (non-temporal) loads and stores, DPP
-// lane permutes.
+// lane permutes, and the counter-based generator of the random draws.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,6 +46,30 @@ constexpr int kQuadBcast1 = 0x55;  // quad_perm [1,1,1,1]
 constexpr int kQuadBcast2 = 0xAA;  // quad_perm [2,2,2,2]
 constexpr int kQuadBcast3 = 0xFF;  // quad_perm [3,3,3,3]
 constexpr int kSwapPairs = 0xB1;   // quad_perm [1,0,3,2]
+
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64-bit products; the high halves are xored with the other counter
+// words and the round key, the words permuted; the key advances by the
+// Weyl increments between rounds.  Each product is one v_mad_u64_u32 and
+// each three-way xor one v_bitop3_b32 (truth table 0x96) on gfx950.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
+        c[0] = n0;
+        c[1] = (uint32_t)p1;
+        c[2] = n2;
+        c[3] = (uint32_t)p0;
+    }
+}
 
 }  // namespace dev
 }  // namespace gcq

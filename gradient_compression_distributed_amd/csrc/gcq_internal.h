@@ -69,6 +69,12 @@ hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint
 // CD-SGD local update (Quant = false) or update fused with the quantizer.
 hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint64_t n, float t,
                         float eta, bool quant, hipStream_t stream);
+// SAPS: T = ceil(2^24 / c), the keep threshold of the 24-bit draw (u c < 1).
+uint32_t saps_threshold(float c);
+hipError_t launch_saps_mask(uint64_t n, float c, uint64_t seed, uint32_t *mask, uint64_t *offs,
+                            hipStream_t stream);
+hipError_t launch_saps_apply(float *x, uint64_t n, const uint32_t *mask, const uint64_t *offs,
+                             float *values, uint64_t cap, bool merge, hipStream_t stream);
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t,
                                  float *acc, hipStream_t stream);
 // maxnorm: bucket scale = largest magnitude (else the L2 norm).

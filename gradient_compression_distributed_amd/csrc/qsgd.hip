@@ -21,29 +21,7 @@ using dev::ld;
 using dev::st;
 using dev::v4f;
 
-// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
-// 32x32->64-bit products; the high halves are xored with the other counter
-// words and the round key, the words permuted; the key advances by the
-// Weyl increments between rounds.  Each product is one v_mad_u64_u32 and
-// each three-way xor one v_bitop3_b32 (truth table 0x96) on gfx950.
-__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1)
-{
-#pragma unroll
-    for (int round = 0; round < 10; ++round) {
-        if (round) {
-            k0 += 0x9E3779B9u;
-            k1 += 0xBB67AE85u;
-        }
-        const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
-        const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
-        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
-        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
-        c[0] = n0;
-        c[1] = (uint32_t)p1;
-        c[2] = n2;
-        c[3] = (uint32_t)p0;
-    }
-}
+using dev::philox4x32_10;
 
 // The four uniforms of elements 4q .. 4q+3: top 24 bits of each output
 // word, times 2^-24 (exact in float32).

@@ -18,6 +18,9 @@
  *     average), Knowl 8 (bucketing, max-norm scaling).
  *   - blog "IMerge修改（Design）": consecutive layers merged into
  *     transmission units (fusion buckets), one unit per message.
+ *   - "Communication-Efficient Decentralized Learning with Sparsification
+ *     and Adaptive Peer Selection": the shared-seed Bernoulli(1/c) mask and
+ *     the single-peer gossip exchange.
  *
  * Conventions shared by every call:
  *   - Array pointers are DEVICE pointers (HIP device memory, e.g. torch
@@ -283,6 +286,65 @@ int qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibb
                          size_t n, uint32_t d, uint32_t s, float *out, void *stream);
 
 /* ------------------------------------------------------------------ */
+/* SAPS: shared-seed random sparsification, single-peer exchange       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * saps_mask -- the sparsification mask of "Communication-Efficient
+ * Decentralized Learning with Sparsification and Adaptive Peer Selection":
+ * entries Bernoulli(1/c) drawn from a seed that every worker shares, so all
+ * workers keep the same components.  Element i is kept when u_i * c < 1
+ * (exactly), u_i = the 24-bit uniform of qsgd_quantize's generator for
+ * (seed, i).
+ *
+ *   n             element count
+ *   c             finite, >= 1 (the compression ratio; 1 keeps everything)
+ *   seed          the shared seed
+ *   mask_words    out, uint32[saps_mask_words(n)], 4-byte aligned; bit j of
+ *                 word w is element 32w + j (bits past n are 0)
+ *   tile_offsets  out, uint64[saps_num_tiles(n) + 1], 8-byte aligned: entry t
+ *                 is the number of kept elements before element 8192 t (an
+ *                 exclusive prefix over 8192-element tiles); the last entry
+ *                 is the total kept count (read it after a synchronize to
+ *                 size the value buffer)
+ *
+ * Errors: GCQ_ERR_PARAM (c), GCQ_ERR_NULL, GCQ_ERR_ALIGN, GCQ_ERR_OVERLAP,
+ * GCQ_ERR_LAUNCH.
+ */
+int saps_mask(size_t n, float c, uint64_t seed, uint32_t *mask_words, uint64_t *tile_offsets,
+              void *stream);
+
+/*
+ * saps_gather -- the components a worker sends: values[r] = x[i_r] for the
+ * kept indices i_0 < i_1 < ... (mask and offsets from saps_mask).  Only
+ * ranks below `capacity` are written (size the buffer with the total count).
+ *
+ *   x         in, float32[n], 4-byte aligned
+ *   values    out, float32[capacity], 4-byte aligned
+ *
+ * Errors: GCQ_ERR_PARAM, GCQ_ERR_NULL, GCQ_ERR_ALIGN, GCQ_ERR_OVERLAP,
+ * GCQ_ERR_LAUNCH.
+ */
+int saps_gather(const float *x, size_t n, const uint32_t *mask_words,
+                const uint64_t *tile_offsets, float *values, size_t capacity, void *stream);
+
+/*
+ * saps_merge -- the receiving side of the single-peer exchange: each row of
+ * the gossip matrix has two non-zero entries and the matrix is doubly
+ * stochastic, read as an equal-weight average: for every kept index i_r
+ * with r < capacity, x[i_r] = (x[i_r] + peer_values[r]) * 0.5 in float32;
+ * other components are unchanged.  The peer used the same seed, so its
+ * values are in the same order.
+ *
+ *   x            in/out, float32[n], 4-byte aligned
+ *   peer_values  in, float32[capacity], 4-byte aligned
+ *
+ * Errors: as saps_gather.
+ */
+int saps_merge(float *x, size_t n, const uint32_t *mask_words, const uint64_t *tile_offsets,
+               const float *peer_values, size_t capacity, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* Sizes and status names (pure host functions, no device access)      */
 /* ------------------------------------------------------------------ */
 
@@ -292,6 +354,10 @@ size_t gc2_packed_words(size_t n);
 size_t qsgd_num_buckets(size_t n, uint32_t d);
 /* ceil(n/8): QSGD nibble words. */
 size_t qsgd_nibble_words(size_t n);
+/* ceil(n/32): SAPS mask words. */
+size_t saps_mask_words(size_t n);
+/* ceil(n/8192): SAPS tiles (saps_mask writes one more offset than this). */
+size_t saps_num_tiles(size_t n);
 /* Static, never-NULL name of a status code. */
 const char *gcq_status_string(int status);
 

@@ -197,6 +197,30 @@ def test_qsgd_maxnorm_and_average_validation(lib):
     assert lib.qsgd_dequant_average(arr(sc), arr(nbs), 3, 0, 512, 7, vp(out), NULL) == OK
 
 
+def test_saps_validation(lib):
+    n = 100_000
+    x, m, o, v = A, A + (1 << 20), A + (2 << 20), A + (3 << 20)
+    assert lib.saps_mask_words(n) == 3125 and lib.saps_mask_words(33) == 2
+    assert lib.saps_num_tiles(n) == 13 and lib.saps_num_tiles(8192) == 1
+    mk = lambda n_, c, m_, o_: lib.saps_mask(n_, F(c), ctypes.c_uint64(5), vp(m_), vp(o_), NULL)
+    for bad in (0.5, 0.0, -2.0, float("nan"), float("inf")):
+        assert mk(n, bad, m, o) == E_PARAM
+    assert mk(n, 100.0, 0, o) == E_NULL
+    assert mk(0, 100.0, m, 0) == E_NULL
+    assert mk(n, 100.0, m + 2, o) == E_ALIGN
+    assert mk(n, 100.0, m, o + 4) == E_ALIGN
+    assert mk(n, 100.0, m, m + 64) == E_OVERLAP
+    g = lambda x_, m_, o_, v_, cap: lib.saps_gather(vp(x_), n, vp(m_), vp(o_), vp(v_), cap, NULL)
+    assert g(0, m, o, v, 10) == E_NULL
+    assert g(x, m, o, 0, 10) == E_NULL
+    assert g(x + 2, m, o, v, 10) == E_ALIGN
+    assert g(x, m, o, x + 400, 10) == E_OVERLAP            # values inside x
+    assert g(x, m, o, m, 10) == E_OVERLAP                  # values over the mask
+    mg = lambda x_, m_, o_, v_, cap: lib.saps_merge(vp(x_), n, vp(m_), vp(o_), vp(v_), cap, NULL)
+    assert mg(x, m, o, x + 4000, 10) == E_OVERLAP         # peer values inside x
+    assert lib.saps_gather(vp(x), 0, vp(m), vp(o), vp(v), 0, NULL) == OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     g = torch.zeros(16)

@@ -1,0 +1,188 @@
+"""GPU parity of the SAPS sparsification (saps_mask, saps_gather, saps_merge)
+against the CPU oracle, bit-exact: mask words, tile offsets and total count,
+gathered values, merged vectors.
+
+"Communication-Efficient Decentralized Learning with Sparsification and
+Adaptive Peer Selection": the shared-seed Bernoulli(1/c) mask, only the kept
+components exchanged, single-peer gossip."""
+import numpy as np
+import pytest
+
+import oracle
+from gradient_compression_distributed_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TILE = 8192
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+def dev(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint32) if a.dtype == np.int32 else a
+
+
+def fbits(a):
+    a = np.ascontiguousarray(a)
+    b = a.view(np.uint32).copy()
+    b[np.isnan(a)] = 0x7FC00000
+    return b
+
+
+def oracle_mask(n, c, seed):
+    """Mask words and tile offsets from the oracle's kept indices."""
+    kept = oracle.saps_gather(np.arange(n, dtype=np.float32), c, seed).astype(np.int64)
+    words = np.zeros((n + 31) // 32, dtype=np.uint64)
+    np.add.at(words, kept // 32, np.left_shift(np.uint64(1), (kept % 32).astype(np.uint64)))
+    ntiles = (n + TILE - 1) // TILE
+    counts = np.bincount(kept // TILE, minlength=ntiles)[:ntiles]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return words.astype(np.uint32), offs, kept
+
+
+def check(gpu, x, c, seed):
+    import torch
+
+    n = x.size
+    mask, offs = gpu.saps_mask(n, c, seed)
+    w_h, o_h, kept = oracle_mask(n, c, seed)
+    assert np.array_equal(host(mask), w_h), (n, c, seed)
+    assert np.array_equal(host(offs), o_h), (n, c, seed)
+    total = gpu.saps_count(offs)
+    assert total == kept.size
+    # gather, with sentinels past the used part of the buffer
+    buf = torch.full((total + 5,), 3.25, device="cuda")
+    gpu.saps_gather(dev(x), mask, offs, values=buf[:total])
+    vals = oracle.saps_gather(x, c, seed)
+    b = host(buf)
+    assert np.array_equal(fbits(b[:total]), fbits(vals)), (n, c)
+    assert np.all(b[total:] == 3.25)
+    # merge a peer's values
+    rs = np.random.default_rng(n % 1000 + 1)
+    peer = rs.standard_normal(total).astype(np.float32)
+    xd = dev(x)
+    gpu.saps_merge(xd, mask, offs, dev(peer))
+    xh = x.copy()
+    oracle.saps_merge(xh, c, seed, peer)
+    assert np.array_equal(fbits(host(xd)), fbits(xh)), (n, c)
+    return mask, offs
+
+
+@pytest.mark.parametrize("c", [1.0, 2.0, 3.5, 100.0, 1e6, 2.0 ** 24, 1e30])
+def test_ratios(gpu, c):
+    say("saps c", c)
+    rs = np.random.default_rng(90)
+    for n in (1, 31, 32, 33, 8191, 8192, 8193, 100_003, 1_000_000):
+        x = rs.standard_normal(n).astype(np.float32)
+        check(gpu, x, c, 1234 + n)
+
+
+def test_ragged_sizes_and_specials(gpu):
+    say("saps ragged sizes")
+    rs = np.random.default_rng(91)
+    sp = np.array([0.0, -0.0, np.nan, np.inf, -np.inf, 1e-45, 3e38], np.float32)
+    for n in list(range(0, 70)) + [TILE * 3 + 17, TILE * 16]:
+        x = rs.standard_normal(n).astype(np.float32)
+        m = rs.random(n) < 0.1
+        x[m] = sp[rs.integers(0, sp.size, m.sum())]
+        if n == 0:
+            mask, offs = gpu.saps_mask(0, 4.0, 1)
+            assert gpu.saps_count(offs) == 0
+            continue
+        check(gpu, x, 4.0, 77 + n)
+
+
+def test_short_capacity_writes_only_what_fits(gpu):
+    import torch
+
+    say("saps capacity")
+    n, c, seed = 200_000, 10.0, 5
+    x = np.random.default_rng(92).standard_normal(n).astype(np.float32)
+    mask, offs = gpu.saps_mask(n, c, seed)
+    total = gpu.saps_count(offs)
+    cap = total // 3
+    buf = torch.full((total,), 7.5, device="cuda")
+    gpu.saps_gather(dev(x), mask, offs, values=buf[:cap])
+    vals = oracle.saps_gather(x, c, seed)
+    b = host(buf)
+    assert np.array_equal(b[:cap], vals[:cap])
+    assert np.all(b[cap:] == 7.5)
+    # merge with a short peer buffer: only the first cap kept components move
+    xd = dev(x)
+    peer = np.full(total, 1.0, np.float32)
+    gpu.saps_merge(xd, mask, offs, dev(peer[:cap]))
+    xh = x.copy()
+    kept = oracle_mask(n, c, seed)[2]
+    xh[kept[:cap]] = (xh[kept[:cap]] + np.float32(1.0)) * np.float32(0.5)
+    assert np.array_equal(host(xd), xh)
+
+
+def test_two_peers_agree_after_exchange(gpu):
+    say("saps exchange")
+    rs = np.random.default_rng(93)
+    n, c, seed = 500_000, 100.0, 2026
+    a, b = rs.standard_normal(n).astype(np.float32), rs.standard_normal(n).astype(np.float32)
+    ad, bd = dev(a), dev(b)
+    mask, offs = gpu.saps_mask(n, c, seed)
+    va, vb = gpu.saps_gather(ad, mask, offs), gpu.saps_gather(bd, mask, offs)
+    gpu.saps_merge(ad, mask, offs, vb)
+    gpu.saps_merge(bd, mask, offs, va)
+    kept = oracle_mask(n, c, seed)[2]
+    ah, bh = host(ad), host(bd)
+    assert np.array_equal(ah[kept], bh[kept])
+    oracle.saps_merge(a, c, seed, host(vb))
+    assert np.array_equal(ah, a)
+
+
+def test_full_size_sampled(gpu):
+    """2^30 elements at c = 100 (the launches the benchmark times): the mask
+    and offsets of sampled tiles, the total, and gathered / merged values
+    there, against the oracle."""
+    import torch
+
+    n, c, seed = 1 << 30, 100.0, wl.qsgd_seed(5)
+    say("saps full size", n)
+    x = torch.empty(n, device="cuda")
+    wl.fill_normal_(x, 8, 1, 1.0)
+    mask, offs = gpu.saps_mask(n, c, seed)
+    total = gpu.saps_count(offs)
+    vals = gpu.saps_gather(x, mask, offs)
+    peer = torch.empty(total, device="cuda")
+    wl.fill_normal_(peer, 8, 2, 1.0)
+    x2 = x.clone()
+    gpu.saps_merge(x2, mask, offs, peer)
+    torch.cuda.synchronize()
+    say("launched, kept", total)
+    mu, sd = n / c, np.sqrt(n / c)
+    assert abs(total - mu) < 6 * sd
+    lib = oracle._load()
+    import ctypes
+    rs = np.random.default_rng(94)
+    o = host(offs)
+    tiles = sorted(set([0, n // TILE - 1] + [int(t) for t in rs.integers(0, n // TILE, 12)]))
+    for t in tiles:
+        e0 = t * TILE
+        kept = np.array([i for i in range(e0, e0 + TILE)
+                         if lib.oracle_saps_keep(seed, i, ctypes.c_float(c))], dtype=np.int64)
+        words = host(mask[e0 // 32:(e0 + TILE) // 32])
+        want = np.zeros(TILE // 32, np.uint64)
+        np.add.at(want, (kept - e0) // 32,
+                  np.left_shift(np.uint64(1), ((kept - e0) % 32).astype(np.uint64)))
+        assert np.array_equal(words, want.astype(np.uint32)), t
+        r0, r1 = int(o[t]), int(o[t + 1])
+        assert r1 - r0 == kept.size, t
+        xs = host(x[e0:e0 + TILE])
+        assert np.array_equal(host(vals[r0:r1]), xs[kept - e0]), t
+        ps = host(peer[r0:r1])
+        want_x = xs.copy()
+        want_x[kept - e0] = (xs[kept - e0] + ps) * np.float32(0.5)
+        assert np.array_equal(host(x2[e0:e0 + TILE]), want_x), t
