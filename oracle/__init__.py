@@ -26,6 +26,9 @@ passage of the pages it follows:
   Efficient Decentralized Learning with Sparsification and Adaptive Peer
   Selection"): the shared-seed Bernoulli(1/c) mask and the single-peer
   exchange.
+* ``omega_length`` / ``qsgd_elias_encode`` / ``qsgd_elias_decode`` -- QSGD
+  summary Knowl 2 (norm, then omega-coded distances between non-zero
+  coordinates with sign and level), Elias' omega code (1975).
 * ``philox4x32_10`` / ``uniform`` -- the SC'11 Philox-4x32 generator.  The
   pages name no random source, so the exact uniform stream is
   "parity unpinned" by the pages; it is pinned only statistically.
@@ -73,6 +76,12 @@ def _load():
     lib.oracle_qsgd_quantize.argtypes = [vp, sz, u32, u32, u64, vp, vp]
     lib.oracle_qsgd_quantize.restype = None
     lib.oracle_qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp]
+    lib.oracle_omega_length.argtypes = [u64]
+    lib.oracle_omega_length.restype = ctypes.c_uint
+    lib.oracle_qsgd_elias_encode.argtypes = [vp, vp, sz, u32, vp, vp, sz]
+    lib.oracle_qsgd_elias_encode.restype = u64
+    lib.oracle_qsgd_elias_decode.argtypes = [vp, vp, sz, u32, vp, vp]
+    lib.oracle_qsgd_elias_decode.restype = None
     lib.oracle_saps_keep.argtypes = [u64, u64, f32]
     lib.oracle_saps_keep.restype = ctypes.c_int
     lib.oracle_saps_gather.argtypes = [vp, sz, f32, u64, vp]
@@ -298,3 +307,36 @@ def saps_merge(x: np.ndarray, c: float, seed: int, peer: np.ndarray) -> int:
     _f32(x, "x"), _f32(peer, "peer")
     return int(lib.oracle_saps_merge(_ptr(x), x.size, ctypes.c_float(c), ctypes.c_uint64(seed),
                                      _ptr(peer)))
+
+
+def omega_length(k: int) -> int:
+    return int(_load().oracle_omega_length(k))
+
+
+def qsgd_elias_encode(norms: np.ndarray, nibbles: np.ndarray, n: int, d: int):
+    """Returns (bit_offsets uint64[nb + 1], words uint32[ceil(total/32)])."""
+    lib = _load()
+    _f32(norms, "norms"), _u32(nibbles, "nibbles")
+    nb = num_buckets(n, d)
+    if norms.size < nb or nibbles.size < nibble_words(n):
+        raise ValueError("inputs too small")
+    offs = np.empty(nb + 1, dtype=np.uint64)
+    cap = nb + (n * 32 + 31) // 32 + 1          # 32 norm bits + at most 32 bits per element
+    out = np.empty(cap, dtype=np.uint32)
+    total = lib.oracle_qsgd_elias_encode(_ptr(norms), _ptr(nibbles), n, d, _ptr(offs), _ptr(out),
+                                         cap)
+    return offs, out[:(total + 31) // 32].copy()
+
+
+def qsgd_elias_decode(words: np.ndarray, bit_offsets: np.ndarray, n: int, d: int):
+    """Returns (norms, nibbles) of the coded buckets."""
+    lib = _load()
+    _u32(words, "words")
+    nb = num_buckets(n, d)
+    offs = np.ascontiguousarray(bit_offsets, dtype=np.uint64)
+    if offs.size < nb + 1:
+        raise ValueError("bit_offsets too small")
+    norms = np.empty(nb, dtype=np.float32)
+    nib = np.empty(nibble_words(n), dtype=np.uint32)
+    lib.oracle_qsgd_elias_decode(_ptr(words), _ptr(offs), n, d, _ptr(norms), _ptr(nib))
+    return norms, nib

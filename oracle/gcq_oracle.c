@@ -24,6 +24,9 @@
  *         Encoding" (chapterpal summary): Knowl 1 (the Q_s operator),
  *         Knowl 2 (the (norm, sign, level) tuple), Knowl 3 (decode and
  *         average), Knowl 8 (bucketing, max-norm scaling).
+ *   [EL]  P. Elias, "Universal codeword sets and representations of the
+ *         integers" (IEEE Trans. Inf. Theory, 1975): the omega code, as used
+ *         by [QS] Knowl 2.
  *   [SA]  "Communication-Efficient Decentralized Learning with Sparsification
  *         and Adaptive Peer Selection": the shared-seed Bernoulli(1/c)
  *         sparsification mask and the single-peer gossip exchange.
@@ -408,4 +411,159 @@ size_t oracle_saps_merge(float *x, size_t n, float c, uint64_t seed, const float
         }
     }
     return k;
+}
+
+/* ------------------------------------------------------------------ */
+/* QSGD message coding with Elias omega codes                          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [EL] omega code of a positive integer k: start from the single bit 0;
+ * while k > 1, put the binary form of k (which starts with a 1) in front
+ * and continue with k = (its number of digits) - 1.  omega(1) = 0,
+ * omega(2) = 100, omega(3) = 110, omega(4) = 101000.
+ */
+static unsigned oracle_bit_length(uint64_t k)
+{
+    unsigned len = 0;
+    while (k) {
+        len++;
+        k >>= 1;
+    }
+    return len;
+}
+
+/* Appends `nbits` low bits of v, most significant first, at bit *pos of out
+ * (bit 31 of a word is its first bit); out must be zeroed. */
+static void oracle_put_bits(uint32_t *out, uint64_t *pos, uint64_t v, unsigned nbits)
+{
+    for (unsigned b = nbits; b-- > 0;) {
+        if ((v >> b) & 1u)
+            out[*pos / 32] |= 1u << (31u - (unsigned)(*pos % 32));
+        (*pos)++;
+    }
+}
+
+static uint32_t oracle_get_bit(const uint32_t *in, uint64_t *pos)
+{
+    uint32_t bit = (in[*pos / 32] >> (31u - (unsigned)(*pos % 32))) & 1u;
+    (*pos)++;
+    return bit;
+}
+
+static void oracle_omega_put(uint32_t *out, uint64_t *pos, uint64_t k)
+{
+    uint64_t groups[64];
+    unsigned lens[64];
+    int ng = 0;
+    while (k > 1) {
+        unsigned len = oracle_bit_length(k);
+        groups[ng] = k;
+        lens[ng] = len;
+        ng++;
+        k = len - 1;
+    }
+    for (int g = ng - 1; g >= 0; g--)      /* the last group found comes first */
+        oracle_put_bits(out, pos, groups[g], lens[g]);
+    oracle_put_bits(out, pos, 0, 1);
+}
+
+static uint64_t oracle_omega_get(const uint32_t *in, uint64_t *pos)
+{
+    uint64_t k = 1;
+    while (oracle_get_bit(in, pos)) {      /* a group: a 1 and k more digits */
+        uint64_t v = 1;
+        for (uint64_t b = 0; b < k; b++)
+            v = (v << 1) | oracle_get_bit(in, pos);
+        k = v;
+    }
+    return k;
+}
+
+/* Code length of omega(k), in bits. */
+unsigned oracle_omega_length(uint64_t k)
+{
+    unsigned len = 1;
+    while (k > 1) {
+        unsigned b = oracle_bit_length(k);
+        len += b;
+        k = b - 1;
+    }
+    return len;
+}
+
+/*
+ * [QS] Knowl 2: a quantized bucket is the tuple (norm, signs, levels); the
+ * norm takes 32 bits and the non-zero coordinates are coded by the omega
+ * code of the distance from the previous non-zero coordinate, with their
+ * sign and their level.  Readings taken (the format is not spelled out): per
+ * bucket, the 32 bits of the float norm, then for each coordinate i (index
+ * within the bucket) whose level is not 0, in order: omega(i - prev) with
+ * prev the previous such index (-1 before the first), one sign bit (1 =
+ * negative), omega(level).  Buckets follow each other with no padding;
+ * bit_offsets[b] is where bucket b starts and bit_offsets[nb] the total
+ * length (the message lengths, which delimit the buckets).  Bits are written
+ * most significant first into 32-bit words.  Signs of level-0 coordinates are
+ * not coded.
+ *
+ * out must hold ceil(total/32) words; it is zeroed here first up to
+ * out_words.  Returns the total length in bits.
+ */
+uint64_t oracle_qsgd_elias_encode(const float *norms, const uint32_t *nibbles, size_t n,
+                                  uint32_t d, uint64_t *bit_offsets, uint32_t *out,
+                                  size_t out_words)
+{
+    size_t nb = (n + d - 1) / d;
+    for (size_t w = 0; w < out_words; w++)
+        out[w] = 0u;
+    uint64_t pos = 0;
+    for (size_t b = 0; b < nb; b++) {
+        bit_offsets[b] = pos;
+        uint32_t normbits;
+        memcpy(&normbits, &norms[b], 4);
+        oracle_put_bits(out, &pos, normbits, 32);
+        size_t lo = b * (size_t)d;
+        size_t hi = lo + d < n ? lo + d : n;
+        int64_t prev = -1;
+        for (size_t i = lo; i < hi; i++) {
+            uint32_t nib = (nibbles[i / 8] >> (28u - 4u * (unsigned)(i % 8))) & 15u;
+            uint32_t level = nib & 7u;
+            if (level == 0)
+                continue;
+            int64_t li = (int64_t)(i - lo);
+            oracle_omega_put(out, &pos, (uint64_t)(li - prev));
+            oracle_put_bits(out, &pos, nib >> 3, 1);
+            oracle_omega_put(out, &pos, level);
+            prev = li;
+        }
+    }
+    bit_offsets[nb] = pos;
+    return pos;
+}
+
+/* The inverse: norms and nibble words from the coded buckets (every
+ * nibble of a coordinate the code does not name is 0). */
+void oracle_qsgd_elias_decode(const uint32_t *in, const uint64_t *bit_offsets, size_t n,
+                              uint32_t d, float *norms, uint32_t *nibbles)
+{
+    size_t nb = (n + d - 1) / d;
+    for (size_t w = 0; w < (n + 7) / 8; w++)
+        nibbles[w] = 0u;
+    for (size_t b = 0; b < nb; b++) {
+        uint64_t pos = bit_offsets[b];
+        uint32_t normbits = 0;
+        for (int k = 0; k < 32; k++)
+            normbits = (normbits << 1) | oracle_get_bit(in, &pos);
+        memcpy(&norms[b], &normbits, 4);
+        size_t lo = b * (size_t)d;
+        int64_t prev = -1;
+        while (pos < bit_offsets[b + 1]) {
+            int64_t li = prev + (int64_t)oracle_omega_get(in, &pos);
+            uint32_t sign = oracle_get_bit(in, &pos);
+            uint32_t level = (uint32_t)oracle_omega_get(in, &pos);
+            size_t i = lo + (size_t)li;
+            nibbles[i / 8] |= ((sign << 3) | level) << (28u - 4u * (unsigned)(i % 8));
+            prev = li;
+        }
+    }
 }
