@@ -267,6 +267,27 @@ def main():
         next_ops["saps_mask"]["config"] = {"c": c_saps, "n": n, "kept": kept}
         del smask, soffs, svals
 
+        # Elias-omega coding of the QSGD output (d = 512, s = 7) and its decode
+        gcq.qsgd_quantize(g, QSGD_D, QSGD_S, wl.qsgd_seed(11), norms=norms, nibbles=nib)
+        eoffs = torch.empty(gcq.qsgd_num_buckets(n, QSGD_D) + 1, dtype=torch.int64, device=dev)
+        ewords = torch.empty(gcq.qsgd_elias_max_words(n, QSGD_D), dtype=torch.int32, device=dev)
+        enc_ms = timed(lambda: gcq.qsgd_elias_encode(norms, nib, n, QSGD_D, offsets=eoffs,
+                                                     out=ewords))
+        coded_bits = int(eoffs[-1].item())
+        nib2 = torch.empty_like(nib)
+        norms2 = torch.empty_like(norms)
+        dec_ms = timed(lambda: gcq.qsgd_elias_decode(ewords, eoffs, n, QSGD_D, norms=norms2,
+                                                     nibbles=nib2))
+        per_msg = 0.5 + 4.0 / QSGD_D
+        for name, ms, bpe in (("qsgd_elias_encode", enc_ms, per_msg + coded_bits / 8 / n),
+                              ("qsgd_elias_decode", dec_ms, coded_bits / 8 / n + per_msg)):
+            gbps = bpe * n / (ms / 1e3) / 1e9
+            next_ops[name] = {"ms": round(ms, 4), "elements_per_s": n / (ms / 1e3),
+                              "GBps": round(gbps, 1), "bytes_per_element": round(bpe, 4)}
+        next_ops["qsgd_elias_encode"]["config"] = {"d": QSGD_D, "s": QSGD_S, "n": n,
+                                                   "coded_bits_per_element": coded_bits / n}
+        del eoffs, ewords, nib2, norms2
+
     copy_gbps = None
     if args.copy_calibration:
         src = grads[0]

@@ -22,6 +22,7 @@ __all__ = [
     "cdsgd_update_quantize", "cdsgd_local_update", "cdsgd_compresses",
     "qsgd_quantize_maxnorm", "qsgd_dequant_average",
     "saps_mask", "saps_gather", "saps_merge", "saps_mask_words", "saps_num_tiles",
+    "qsgd_elias_encode", "qsgd_elias_decode", "qsgd_elias_max_words",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,12 @@ def load():
     lib.qsgd_dequant_average.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), u32, sz, u32,
                                          u32, vp, vp]
     lib.qsgd_dequant_average.restype = i32
+    lib.qsgd_elias_max_words.argtypes = [sz, u32]
+    lib.qsgd_elias_max_words.restype = sz
+    lib.qsgd_elias_encode.argtypes = [vp, vp, sz, u32, vp, vp, sz, vp]
+    lib.qsgd_elias_encode.restype = i32
+    lib.qsgd_elias_decode.argtypes = [vp, sz, vp, sz, u32, vp, vp, vp]
+    lib.qsgd_elias_decode.restype = i32
     lib.saps_mask.argtypes = [sz, f32, u64, vp, vp, vp]
     lib.saps_mask.restype = i32
     lib.saps_gather.argtypes = [vp, sz, vp, vp, vp, sz, vp]
@@ -407,3 +414,48 @@ def saps_merge(x, mask, offsets, peer_values):
     _dev(peer_values, torch.float32, "peer_values")
     _check(lib.saps_merge(_ptr(x), x.numel(), _ptr(mask), _ptr(offsets), _ptr(peer_values),
                           peer_values.numel(), _stream(x.device)), "saps_merge")
+
+
+# ------------------------------------------------------- QSGD Elias coding
+def qsgd_elias_max_words(n: int, d: int) -> int:
+    return int(load().qsgd_elias_max_words(n, d))
+
+
+def qsgd_elias_encode(norms, nibbles, n: int, d: int, offsets=None, out=None):
+    """Elias-omega coded buckets: returns (bit offsets int64[nb + 1], words
+    int32[capacity]); the coded length in bits is the last offset."""
+    import torch
+
+    lib = load()
+    nb = qsgd_num_buckets(n, d)
+    _dev(norms, torch.float32, "norms", nb)
+    _dev(nibbles, torch.int32, "nibbles", qsgd_nibble_words(n))
+    if offsets is None:
+        offsets = torch.empty(nb + 1, dtype=torch.int64, device=norms.device)
+    if out is None:
+        out = torch.empty(max(qsgd_elias_max_words(n, d), 1), dtype=torch.int32,
+                          device=norms.device)
+    _dev(offsets, torch.int64, "offsets", nb + 1)
+    _dev(out, torch.int32, "out")
+    _check(lib.qsgd_elias_encode(_ptr(norms), _ptr(nibbles), n, d, _ptr(offsets), _ptr(out),
+                                 out.numel(), _stream(out.device)), "qsgd_elias_encode")
+    return offsets, out
+
+
+def qsgd_elias_decode(words, offsets, n: int, d: int, norms=None, nibbles=None):
+    """Returns (norms, nibbles) of Elias-coded buckets."""
+    import torch
+
+    lib = load()
+    nb = qsgd_num_buckets(n, d)
+    _dev(words, torch.int32, "words")
+    _dev(offsets, torch.int64, "offsets", nb + 1)
+    if norms is None:
+        norms = torch.empty(nb, dtype=torch.float32, device=words.device)
+    if nibbles is None:
+        nibbles = torch.empty(qsgd_nibble_words(n), dtype=torch.int32, device=words.device)
+    _dev(norms, torch.float32, "norms", nb)
+    _dev(nibbles, torch.int32, "nibbles", qsgd_nibble_words(n))
+    _check(lib.qsgd_elias_decode(_ptr(words), words.numel(), _ptr(offsets), n, d, _ptr(norms),
+                                 _ptr(nibbles), _stream(words.device)), "qsgd_elias_decode")
+    return norms, nibbles

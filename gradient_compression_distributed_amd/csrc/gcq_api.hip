@@ -430,6 +430,58 @@ int qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibb
         gcq::launch_qsgd_average(ms, K, n, d, s, out, (hipStream_t)stream));
 }
 
+static bool elias_d_ok(uint32_t d) { return d >= 8 && d <= 2048 && d % 8 == 0; }
+
+size_t qsgd_elias_max_words(size_t n, uint32_t d)
+{
+    return elias_d_ok(d) && n <= kMaxElems ? (size_t)gcq::elias_max_words(n, d) : 0;
+}
+
+int qsgd_elias_encode(const float *norms, const uint32_t *nibbles, size_t n, uint32_t d,
+                      uint64_t *bit_offsets, uint32_t *out_words, size_t capacity_words,
+                      void *stream)
+{
+    if (!elias_d_ok(d) || n > kMaxElems || capacity_words > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (!bit_offsets || (n && (!norms || !nibbles || (capacity_words && !out_words))))
+        return GCQ_ERR_NULL;
+    if (!aligned(norms, 4) || !aligned(nibbles, 4) || !aligned(bit_offsets, 8) ||
+        !aligned(out_words, 4))
+        return GCQ_ERR_ALIGN;
+    const size_t nb = qsgd_num_buckets(n, d);
+    std::vector<Range> ranges = {range(norms, nb * 4, false),
+                                 range(nibbles, qsgd_nibble_words(n) * 4, false),
+                                 range(bit_offsets, (nb + 1) * 8, true),
+                                 range(out_words, capacity_words * 4, true)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(gcq::launch_elias_encode(norms, nibbles, n, d, bit_offsets, out_words,
+                                                  capacity_words, (hipStream_t)stream));
+}
+
+int qsgd_elias_decode(const uint32_t *in_words, size_t in_count, const uint64_t *bit_offsets,
+                      size_t n, uint32_t d, float *norms, uint32_t *nibbles, void *stream)
+{
+    if (!elias_d_ok(d) || n > kMaxElems || in_count > kMaxElems)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!bit_offsets || !norms || !nibbles || (in_count && !in_words))
+        return GCQ_ERR_NULL;
+    if (!aligned(in_words, 4) || !aligned(bit_offsets, 8) || !aligned(norms, 4) ||
+        !aligned(nibbles, 4))
+        return GCQ_ERR_ALIGN;
+    const size_t nb = qsgd_num_buckets(n, d);
+    std::vector<Range> ranges = {range(in_words, in_count * 4, false),
+                                 range(bit_offsets, (nb + 1) * 8, false),
+                                 range(norms, nb * 4, true),
+                                 range(nibbles, qsgd_nibble_words(n) * 4, true)};
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(gcq::launch_elias_decode(in_words, bit_offsets, n, d, in_count, norms,
+                                                  nibbles, (hipStream_t)stream));
+}
+
 size_t saps_mask_words(size_t n) { return n / 32 + (n % 32 != 0); }
 
 size_t saps_num_tiles(size_t n) { return n / 8192 + (n % 8192 != 0); }

@@ -69,6 +69,15 @@ hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint
 // CD-SGD local update (Quant = false) or update fused with the quantizer.
 hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint64_t n, float t,
                         float eta, bool quant, hipStream_t stream);
+// In place: a[0..count) -> exclusive prefix sums, a[count] = the total.
+hipError_t launch_exclusive_scan_u64(uint64_t *a, uint64_t count, hipStream_t stream);
+// Elias-omega coding of QSGD buckets (d a multiple of 8, at most 2048).
+uint64_t elias_max_words(uint64_t n, uint32_t d);
+hipError_t launch_elias_encode(const float *norms, const uint32_t *nibbles, uint64_t n, uint32_t d,
+                               uint64_t *offs, uint32_t *out, uint64_t cap, hipStream_t stream);
+hipError_t launch_elias_decode(const uint32_t *in, const uint64_t *offs, uint64_t n, uint32_t d,
+                               uint64_t in_words, float *norms, uint32_t *nibbles,
+                               hipStream_t stream);
 // SAPS: T = ceil(2^24 / c), the keep threshold of the 24-bit draw (u c < 1).
 uint32_t saps_threshold(float c);
 hipError_t launch_saps_mask(uint64_t n, float c, uint64_t seed, uint32_t *mask, uint64_t *offs,

@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kSapsThreads) void saps_mask_kernel(uint64_t n, uin
     }
 }
 
-// In place: offs[0..ntiles) counts -> exclusive offsets, offs[ntiles] = total.
-// One workgroup of 1024 threads, 16 consecutive entries per thread per pass.
+// In place: offs[0..ntiles) counts -> exclusive offsets, offs[ntiles] = total
+// (also the scan behind the Elias coder's bucket offsets).  One workgroup of
+// 1024 threads, 16 consecutive entries per thread per pass.
 __global__ __launch_bounds__(1024) void saps_scan_kernel(uint64_t *__restrict__ offs,
                                                           uint64_t ntiles)
 {
@@ -190,7 +191,12 @@ hipError_t launch_saps_mask(uint64_t n, float c, uint64_t seed, uint32_t *mask, 
         if (e != hipSuccess)
             return e;
     }
-    saps_scan_kernel<<<1, 1024, 0, stream>>>(offs, ntiles);
+    return launch_exclusive_scan_u64(offs, ntiles, stream);
+}
+
+hipError_t launch_exclusive_scan_u64(uint64_t *a, uint64_t count, hipStream_t stream)
+{
+    saps_scan_kernel<<<1, 1024, 0, stream>>>(a, count);
     return hipGetLastError();
 }
 

@@ -14,8 +14,8 @@
  *     compression read the same gradient buffer).
  *   - "QSGD: Communication-Efficient SGD via Gradient Quantization and
  *     Encoding" (chapterpal summary): Knowl 1 (Q_s), Knowl 2 (the
- *     (norm, sign, level) tuple), Knowl 3 (encode, broadcast, decode,
- *     average), Knowl 8 (bucketing, max-norm scaling).
+ *     (norm, sign, level) tuple and its Elias coding), Knowl 3 (encode,
+ *     broadcast, decode, average), Knowl 8 (bucketing, max-norm scaling).
  *   - blog "IMerge修改（Design）": consecutive layers merged into
  *     transmission units (fusion buckets), one unit per message.
  *   - "Communication-Efficient Decentralized Learning with Sparsification
@@ -285,6 +285,43 @@ int qsgd_quantize_maxnorm(const float *g, size_t n, uint32_t d, uint32_t s, uint
 int qsgd_dequant_average(const float *const *scales, const uint32_t *const *nibbles, uint32_t K,
                          size_t n, uint32_t d, uint32_t s, float *out, void *stream);
 
+/*
+ * qsgd_elias_encode -- the QSGD summary's Knowl 2 coding of quantized
+ * buckets with Elias omega codes (P. Elias, "Universal codeword sets and
+ * representations of the integers", 1975: omega(1) = 0; for k > 1 the
+ * binary digits of k, preceded by omega-style groups for its length - 1,
+ * then a final 0).  Per bucket: the 32 bits of the norm, then for every
+ * coordinate i (index within the bucket) whose level is not 0, in order:
+ * omega(i - prev) with prev the previous such index (-1 before the first),
+ * one sign bit (1 = negative), omega(level).  Buckets follow each other
+ * without padding; bits are written most significant first into 32-bit
+ * words.  Signs of level-0 coordinates are not coded.
+ *
+ *   norms, nibbles  a qsgd_quantize output (device), 4-byte aligned
+ *   n, d            d a multiple of 8, 8 <= d <= 2048
+ *   bit_offsets     out, uint64[ceil(n/d) + 1], 8-byte aligned: where bucket
+ *                   b starts; the last entry is the total length in bits
+ *   out_words       out, uint32[capacity_words]; words past the capacity are
+ *                   not written (qsgd_elias_max_words bounds what is needed)
+ *
+ * Errors: GCQ_ERR_PARAM (d), GCQ_ERR_NULL, GCQ_ERR_ALIGN, GCQ_ERR_OVERLAP,
+ * GCQ_ERR_LAUNCH.
+ */
+int qsgd_elias_encode(const float *norms, const uint32_t *nibbles, size_t n, uint32_t d,
+                      uint64_t *bit_offsets, uint32_t *out_words, size_t capacity_words,
+                      void *stream);
+
+/*
+ * qsgd_elias_decode -- the inverse: norms and nibble words from coded buckets
+ * (in_words holds in_count words; nothing past them or past a bucket's end
+ * is read, and a malformed bucket stops at its last whole coordinate).
+ * Coordinates the code does not name get nibble 0.
+ *
+ * Errors: as qsgd_elias_encode.
+ */
+int qsgd_elias_decode(const uint32_t *in_words, size_t in_count, const uint64_t *bit_offsets,
+                      size_t n, uint32_t d, float *norms, uint32_t *nibbles, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* SAPS: shared-seed random sparsification, single-peer exchange       */
 /* ------------------------------------------------------------------ */
@@ -354,6 +391,8 @@ size_t gc2_packed_words(size_t n);
 size_t qsgd_num_buckets(size_t n, uint32_t d);
 /* ceil(n/8): QSGD nibble words. */
 size_t qsgd_nibble_words(size_t n);
+/* An upper bound of the words qsgd_elias_encode writes (0 for a bad d). */
+size_t qsgd_elias_max_words(size_t n, uint32_t d);
 /* ceil(n/32): SAPS mask words. */
 size_t saps_mask_words(size_t n);
 /* ceil(n/8192): SAPS tiles (saps_mask writes one more offset than this). */

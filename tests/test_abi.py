@@ -221,6 +221,29 @@ def test_saps_validation(lib):
     assert lib.saps_gather(vp(x), 0, vp(m), vp(o), vp(v), 0, NULL) == OK
 
 
+def test_elias_validation(lib):
+    n = 4096
+    nm, nb, of, out = A, A + (1 << 20), A + (2 << 20), A + (3 << 20)
+    assert lib.qsgd_elias_max_words(n, 7) == 0 and lib.qsgd_elias_max_words(n, 4096) == 0
+    assert lib.qsgd_elias_max_words(n, 512) > n * 24 // 32
+    e = lambda d, nm_, nb_, of_, o_, cap: lib.qsgd_elias_encode(vp(nm_), vp(nb_), n, d, vp(of_),
+                                                                vp(o_), cap, NULL)
+    for bad_d in (0, 4, 12, 2056, 4096):
+        assert e(bad_d, nm, nb, of, out, 100) == E_PARAM
+    assert e(512, 0, nb, of, out, 100) == E_NULL
+    assert e(512, nm, nb, 0, out, 100) == E_NULL
+    assert e(512, nm, nb, of + 4, out, 100) == E_ALIGN
+    assert e(512, nm, nb, of, out + 2, 100) == E_ALIGN
+    assert e(512, nm, nb, of, nb + 64, 100) == E_OVERLAP        # words over the nibbles
+    assert e(512, nm, nb, nm, out, 100) == E_OVERLAP            # offsets over the norms
+    dd = lambda d, i_, cnt, of_, nm_, nb_: lib.qsgd_elias_decode(vp(i_), cnt, vp(of_), n, d,
+                                                                 vp(nm_), vp(nb_), NULL)
+    assert dd(100, out, 10, of, nm, nb) == E_PARAM
+    assert dd(512, out, 10, of, 0, nb) == E_NULL
+    assert dd(512, out, 10, of, nm, out + 4) == E_OVERLAP       # nibbles over the input
+    assert lib.qsgd_elias_decode(vp(out), 10, vp(of), 0, 512, vp(nm), vp(nb), NULL) == OK
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     g = torch.zeros(16)
