@@ -231,20 +231,20 @@ def main():
         # QSGD with max-norm bucket scales, and the 16-worker decode-average
         mx_ms = timed(lambda: gcq.qsgd_quantize_maxnorm(g, QSGD_D, QSGD_S, wl.qsgd_seed(7),
                                                         scales=norms, nibbles=nib))
-        K = W_WORKERS
-        msgs = [gcq.qsgd_quantize(g, QSGD_D, QSGD_S, wl.qsgd_seed(200 + k)) for k in range(K)]
+        Kw = W_WORKERS
+        msgs = [gcq.qsgd_quantize(g, QSGD_D, QSGD_S, wl.qsgd_seed(200 + k)) for k in range(Kw)]
         torch.cuda.synchronize()
         avg_ms = timed(lambda: gcq.qsgd_dequant_average([m[0] for m in msgs], [m[1] for m in msgs],
                                                         n, QSGD_D, QSGD_S, out=qout))
         del msgs
         per_msg = 0.5 + 4.0 / QSGD_D
         for name, ms, bpe in (("qsgd_quantize_maxnorm", mx_ms, 4.0 + per_msg),
-                              ("qsgd_dequant_average", avg_ms, K * per_msg + 4.0)):
+                              ("qsgd_dequant_average", avg_ms, Kw * per_msg + 4.0)):
             gbps = bpe * n / (ms / 1e3) / 1e9
             next_ops[name] = {"ms": round(ms, 4), "elements_per_s": n / (ms / 1e3),
                               "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                               "bytes_per_element": round(bpe, 4)}
-        next_ops["qsgd_dequant_average"]["config"] = {"K": K, "d": QSGD_D, "s": QSGD_S, "n": n}
+        next_ops["qsgd_dequant_average"]["config"] = {"K": Kw, "d": QSGD_D, "s": QSGD_S, "n": n}
 
         # SAPS shared-seed sparsification at c = 100 (99% of the components
         # dropped): mask (+ offsets), gather of the kept components, merge of a
