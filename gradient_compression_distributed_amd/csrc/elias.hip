@@ -191,25 +191,39 @@ __global__ __launch_bounds__(kWave) void elias_write_kernel(const float *__restr
     }
 }
 
-// Sequential decode of one bucket per thread; reads never pass the bucket's
-// end or the input, and a code that would is dropped (the bucket stops).
+// Sequential decode of one bucket per thread.  The bits stream through a
+// 64-bit register window refilled a word at a time (one load per 32 bits
+// consumed); the bucket's nibble words are built in a register and stored
+// once each.  Nothing past the bucket's end or the input is read; a code
+// that would run past the end stops the bucket (it then keeps the
+// coordinates decoded so far).
 struct BitReader {
     const uint32_t *in;
-    uint64_t pos, end;
+    uint64_t word;        // next word to load
+    uint64_t left;        // bits of the bucket not yet consumed
+    uint64_t buf;         // window, next bit in bit 63
+    uint32_t avail;       // valid bits in the window
     bool ok;
+
+    __device__ void refill()
+    {
+        while (avail <= 32u && (uint64_t)avail < left) {
+            buf |= (uint64_t)in[word++] << (32u - avail);
+            avail += 32u;
+        }
+    }
     __device__ uint32_t get(uint32_t nbits)   // 1..32 bits
     {
-        if (!ok || pos + nbits > end) {
+        if (!ok || nbits > left) {
             ok = false;
             return 0u;
         }
-        const uint64_t w = pos >> 5;
-        const uint32_t o = (uint32_t)(pos & 31u);
-        uint64_t v = (uint64_t)in[w] << 32;
-        if (o + nbits > 32u)
-            v |= in[w + 1];
-        pos += nbits;
-        return (uint32_t)((v << o) >> (64u - nbits));
+        refill();
+        const uint32_t v = (uint32_t)(buf >> (64u - nbits));
+        buf <<= nbits;
+        avail -= nbits;
+        left -= nbits;
+        return v;
     }
     __device__ uint32_t omega()
     {
@@ -233,24 +247,43 @@ __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
     for (uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
         const uint64_t lo = b * d;
         const uint32_t blen = (uint32_t)(lo + d < n ? d : n - lo);
-        for (uint32_t w = 0; w < (blen + 7u) / 8u; ++w)
-            nibbles[(lo >> 3) + w] = 0u;
-        uint64_t end = offs[b + 1];
+        const uint32_t nw = (blen + 7u) / 8u;
+        uint32_t *nib = nibbles + (lo >> 3);
+        uint64_t start = offs[b], end = offs[b + 1];
         if (end > in_words * 32u)
             end = in_words * 32u;
-        BitReader r{in, offs[b], end, true};
-        const uint32_t normbits = r.get(32);
-        norms[b] = __uint_as_float(normbits);
+        if (start > end)
+            start = end;
+        BitReader r{in, start >> 5, end - start, 0u, 0u, true};
+        // the first word may begin mid-word: load it and drop the bits before
+        // the bucket
+        const uint32_t skip = (uint32_t)(start & 31u);
+        if (end > start) {
+            r.buf = (uint64_t)in[r.word++] << 32;
+            r.avail = 32u;
+            r.buf <<= skip;
+            r.avail -= skip;
+        }
+        norms[b] = __uint_as_float(r.get(32));
         int64_t prev = -1;
-        while (r.ok && r.pos < r.end) {
+        uint32_t cur = 0, cur_w = 0;   // nibble word being built, and its index
+        while (r.ok && r.left) {
             const int64_t li = prev + (int64_t)r.omega();
             const uint32_t sign = r.get(1);
             const uint32_t level = r.omega();
             if (!r.ok || li >= (int64_t)blen || level > 7u)
                 break;
-            const uint64_t i = lo + (uint64_t)li;
-            nibbles[i >> 3] |= ((sign << 3) | level) << (28u - 4u * (uint32_t)(i & 7u));
+            const uint32_t w = (uint32_t)li >> 3;
+            while (cur_w < w) {            // words before this coordinate are done
+                nib[cur_w++] = cur;
+                cur = 0;
+            }
+            cur |= ((sign << 3) | level) << (28u - 4u * ((uint32_t)li & 7u));
             prev = li;
+        }
+        while (cur_w < nw) {
+            nib[cur_w++] = cur;
+            cur = 0;
         }
     }
 }

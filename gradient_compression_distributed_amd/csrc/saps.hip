@@ -8,8 +8,7 @@
 //             quantizer's stream), keeps element i when U_i < T with
 //             T = ceil(2^24 / c) (exactly u_i c < 1), writes one 32-bit mask
 //             word (bit j = element 32w + j) and the tile's kept count;
-//   scan   -- one workgroup turns the tile counts into exclusive offsets
-//             (and the total);
+//   scan   -- the tile counts become exclusive offsets (and the total);
 //   apply  -- per tile, a block scan of the threads' popcounts gives each
 //             thread its first rank; it then gathers x at its set bits into
 //             values[rank], or merges a peer's values there.  Only the cache
@@ -84,45 +83,102 @@ __global__ __launch_bounds__(kSapsThreads) void saps_mask_kernel(uint64_t n, uin
     }
 }
 
-// In place: offs[0..ntiles) counts -> exclusive offsets, offs[ntiles] = total
-// (also the scan behind the Elias coder's bucket offsets).  One workgroup of
-// 1024 threads, 16 consecutive entries per thread per pass.
-__global__ __launch_bounds__(1024) void saps_scan_kernel(uint64_t *__restrict__ offs,
-                                                          uint64_t ntiles)
+// In-place exclusive scan of a[0..count) with a[count] = the total (the SAPS
+// tile offsets and the Elias coder's bucket offsets), in three passes and no
+// workspace, over chunks of kScanChunk entries:
+//   sums  -- each chunk's sum replaces its last entry (that entry's own value
+//            is never needed again: no exclusive prefix includes it);
+//   top   -- one workgroup scans those last entries (exclusive, in place)
+//            and writes the total;
+//   local -- each chunk scans its other entries from its offset, and its
+//            last entry gets the offset plus all of them.
+constexpr uint32_t kScanThreads = 1024;
+constexpr uint64_t kScanChunk = 8u * kScanThreads;
+
+__device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t *part,
+                                                          uint64_t &total)
 {
-    __shared__ uint64_t part[1024];
     const uint32_t tid = threadIdx.x;
-    uint64_t carry = 0;
-    for (uint64_t base = 0; base < ntiles; base += 1024u * 16u) {
-        uint64_t v[16];
-        uint64_t local = 0;
-#pragma unroll
-        for (uint32_t j = 0; j < 16; ++j) {
-            const uint64_t idx = base + (uint64_t)tid * 16u + j;
-            v[j] = idx < ntiles ? offs[idx] : 0u;
-            local += v[j];
-        }
-        part[tid] = local;
+    part[tid] = v;
+    __syncthreads();
+    for (uint32_t off = 1; off < kScanThreads; off <<= 1) {
+        const uint64_t t = tid >= off ? part[tid - off] : 0u;
         __syncthreads();
-        for (uint32_t off = 1; off < 1024; off <<= 1) {
-            const uint64_t t = tid >= off ? part[tid - off] : 0u;
-            __syncthreads();
-            part[tid] += t;
-            __syncthreads();
-        }
-        uint64_t excl = carry + part[tid] - local;
-#pragma unroll
-        for (uint32_t j = 0; j < 16; ++j) {
-            const uint64_t idx = base + (uint64_t)tid * 16u + j;
-            if (idx < ntiles)
-                offs[idx] = excl;
-            excl += v[j];
-        }
-        carry += part[1023];
+        part[tid] += t;
         __syncthreads();
     }
-    if (tid == 0)
-        offs[ntiles] = carry;
+    total = part[kScanThreads - 1];
+    const uint64_t excl = part[tid] - v;
+    __syncthreads();
+    return excl;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_sums_kernel(uint64_t *__restrict__ a,
+                                                                  uint64_t count)
+{
+    __shared__ uint64_t part[kScanThreads];
+    const uint64_t c0 = (uint64_t)blockIdx.x * kScanChunk;
+    const uint64_t c1 = c0 + kScanChunk < count ? c0 + kScanChunk : count;
+    uint64_t local = 0;
+    for (uint64_t i = c0 + threadIdx.x; i < c1; i += kScanThreads)
+        local += a[i];
+    uint64_t total;
+    (void)block_exclusive_scan(local, part, total);
+    if (threadIdx.x == 0)
+        a[c1 - 1] = total;
+}
+
+// Exclusive scan of the chunks' last entries, one workgroup, with the total
+// written to a[count].
+__global__ __launch_bounds__(kScanThreads) void scan_top_kernel(uint64_t *__restrict__ a,
+                                                                 uint64_t count, uint64_t nchunks)
+{
+    __shared__ uint64_t part[kScanThreads];
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < nchunks; base += kScanThreads) {
+        const uint64_t c = base + threadIdx.x;
+        const uint64_t idx = c < nchunks ? ((c + 1) * kScanChunk < count ? (c + 1) * kScanChunk
+                                                                          : count) - 1
+                                         : 0;
+        const uint64_t v = c < nchunks ? a[idx] : 0u;
+        uint64_t total;
+        const uint64_t excl = block_exclusive_scan(v, part, total);
+        if (c < nchunks)
+            a[idx] = carry + excl;
+        carry += total;
+    }
+    if (threadIdx.x == 0)
+        a[count] = carry;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_local_kernel(uint64_t *__restrict__ a,
+                                                                   uint64_t count)
+{
+    __shared__ uint64_t part[kScanThreads];
+    __shared__ uint64_t offset;
+    const uint64_t c0 = (uint64_t)blockIdx.x * kScanChunk;
+    const uint64_t c1 = c0 + kScanChunk < count ? c0 + kScanChunk : count;
+    if (threadIdx.x == 0)
+        offset = a[c1 - 1];
+    // thread t owns entries c0 + 8t .. +7; the chunk's last entry counts as 0
+    uint64_t v[8];
+    uint64_t local = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+        const uint64_t i = c0 + 8u * threadIdx.x + j;
+        v[j] = i < c1 - 1 ? a[i] : 0u;
+        local += v[j];
+    }
+    uint64_t total;
+    uint64_t excl = block_exclusive_scan(local, part, total);   // its barriers order `offset`
+    excl += offset;
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+        const uint64_t i = c0 + 8u * threadIdx.x + j;
+        if (i < c1)
+            a[i] = excl;
+        excl += v[j];
+    }
 }
 
 // Merge = false: values[rank] = x[i] for every kept i (rank < cap).
@@ -196,7 +252,15 @@ hipError_t launch_saps_mask(uint64_t n, float c, uint64_t seed, uint32_t *mask, 
 
 hipError_t launch_exclusive_scan_u64(uint64_t *a, uint64_t count, hipStream_t stream)
 {
-    saps_scan_kernel<<<1, 1024, 0, stream>>>(a, count);
+    const uint64_t nchunks = (count + kScanChunk - 1) / kScanChunk;
+    if (nchunks) {
+        if (nchunks > 0x7FFFFFFFu)
+            return hipErrorInvalidValue;
+        scan_sums_kernel<<<(uint32_t)nchunks, kScanThreads, 0, stream>>>(a, count);
+    }
+    scan_top_kernel<<<1, kScanThreads, 0, stream>>>(a, count, nchunks);
+    if (nchunks)
+        scan_local_kernel<<<(uint32_t)nchunks, kScanThreads, 0, stream>>>(a, count);
     return hipGetLastError();
 }
 

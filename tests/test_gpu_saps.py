@@ -186,3 +186,19 @@ def test_full_size_sampled(gpu):
         want_x = xs.copy()
         want_x[kept - e0] = (xs[kept - e0] + ps) * np.float32(0.5)
         assert np.array_equal(host(x2[e0:e0 + TILE]), want_x), t
+
+
+def test_offsets_across_scan_chunks(gpu):
+    # 9000 tiles: the offsets scan runs over more than one 8192-entry chunk,
+    # the second one partial
+    n, c, seed = 9000 * TILE + 5, 100.0, 31337
+    say("saps offsets over", (n + TILE - 1) // TILE, "tiles")
+    mask, offs = gpu.saps_mask(n, c, seed)
+    # gather each element's tile number (exact in float32, unlike an index
+    # past 2^24): the tiles of the kept elements, in order
+    tile_of = (np.arange(n, dtype=np.int64) // TILE).astype(np.float32)
+    kept_tiles = oracle.saps_gather(tile_of, c, seed).astype(np.int64)
+    ntiles = (n + TILE - 1) // TILE
+    counts = np.bincount(kept_tiles, minlength=ntiles)[:ntiles]
+    want = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    assert np.array_equal(host(offs), want)
