@@ -359,7 +359,9 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_levels_generic_kernel(
     }
 }
 
-// Decode (Knowl 3): out = +-((norm * level) / s).  A wavefront owns 1024
+// Decode (Knowl 3): out = +-((norm * level) / s), one division per element
+// (buckets shorter than 341 elements; longer ones take the lane-table kernel
+// below, which computes the same quotients).  A wavefront owns 1024
 // consecutive outputs; lane L decodes elements 256q + 4L .. +3 (q = 0..3),
 // so every 16-byte store instruction of the wave writes 1 KiB of
 // consecutive memory.  Lanes 2m and 2m+1 read the two halves of one nibble
@@ -404,6 +406,88 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_kernel(
                 const float m = (Pow2 ? nrm[q][0] : nrm[q][j]) * (float)(nb & 7u);
                 const float v = m / sf;
                 o[q][j] = (nb & 8u) ? -v : v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (e[q] + 4 <= n) {
+                v4f x;
+                x.x = o[q][0];
+                x.y = o[q][1];
+                x.z = o[q][2];
+                x.w = o[q][3];
+                st<NT>(reinterpret_cast<v4f *>(out + e[q]), x);
+            } else {
+                for (int j = 0; j < 4; ++j)
+                    if (e[q] + j < n)
+                        out[e[q] + j] = o[q][j];
+            }
+        }
+    }
+}
+
+// Decode through a lane table, for 341 <= d <= 2^30: the 1024 outputs of a
+// wavefront touch at most 4 buckets (rel + 1023 < 4d for every offset rel < d
+// of the tile into its first bucket), so the 64 values +-((norm * level) / s)
+// of those buckets, slot L / 16 and nibble L % 16, are one per lane.  Each
+// lane computes its one quotient exactly as the per-element decode does (-0
+// for a sign-bit-set level 0 included), and every output is fetched from the
+// lane that holds it with ds_bpermute: per element a nibble extract, an
+// address and a cross-lane read, no division.  Tile layout, loads and
+// stores as above.
+template <bool Pow2, bool NT>
+__global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_lanes_kernel(
+    const float *__restrict__ norms, const uint32_t *__restrict__ nib, uint64_t n, uint32_t d,
+    uint32_t dshift, uint32_t s, float *__restrict__ out)
+{
+    const float sf = (float)s;
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
+    const uint64_t nbuckets = (n + d - 1) / d;
+    const uint64_t wstride = (uint64_t)gridDim.x * kBlockWaves;
+    const uint32_t tnib = lane & 15u;
+    const float tlev = (float)(tnib & 7u);
+    for (uint64_t t = (uint64_t)blockIdx.x * kBlockWaves + threadIdx.x / kWave; t < ntiles;
+         t += wstride) {
+        const uint64_t et = t * kWaveElems;
+        const uint64_t b0 = Pow2 ? et >> dshift : et / d;
+        const uint32_t rel0 = (uint32_t)(et - b0 * d);   // < d
+        uint64_t e[4];
+        uint32_t word[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            e[q] = et + 256u * q + 4u * lane;
+            const uint64_t es = e[q] < n ? e[q] : 0;
+            word[q] = ld<NT>(nib + (es >> 3));
+        }
+        const uint64_t bl = b0 + (lane >> 4);
+        const float nrm = bl < nbuckets ? norms[bl] : 0.0f;
+        const float m = nrm * tlev;
+        const float v = m / sf;
+        const int tv = __float_as_int((tnib & 8u) ? -v : v);
+        float o[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t h = (lane & 1u) ? (word[q] & 0xFFFFu) : (word[q] >> 16);
+            const uint32_t rel = rel0 + 256u * q + 4u * lane;
+            uint32_t slot[4];
+            if constexpr (Pow2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    slot[j] = rel >> dshift;   // d >= 512: one bucket per 4 elements
+            } else {
+                const uint32_t s0 = (rel >= d ? 1u : 0u) + (rel >= 2u * d ? 1u : 0u) +
+                                    (rel >= 3u * d ? 1u : 0u);
+                const uint32_t brk = (s0 + 1u) * d - rel;   // first j in the next bucket
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    slot[j] = s0 + ((uint32_t)j >= brk ? 1u : 0u);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t nb = (h >> (12 - 4 * j)) & 0xFu;
+                const int addr = (int)(((slot[j] << 4) | nb) << 2);   // < 256 for slot <= 3
+                o[q][j] = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, tv));
             }
         }
 #pragma unroll
@@ -720,9 +804,16 @@ hipError_t launch_qsgd_dequant(const float *norms, const uint32_t *nibbles, uint
         grid_for((ntiles + kBlockWaves - 1) / kBlockWaves, tu.qsgd_dequant_blocks_per_cu);
     const bool pow2 = d >= 4 && (d & (d - 1)) == 0;
     const uint32_t dshift = pow2 ? (uint32_t)__builtin_ctz(d) : 0u;
+    const bool lanes = d >= 341 && d <= (1u << 30);
 #define GCQ_DQ(P, NT)                                                                           \
-    qsgd_dequant_kernel<P, NT><<<grid, kBlockThreads, 0, stream>>>(norms, nibbles, n, d, dshift, s, \
-                                                                   out)
+    do {                                                                                        \
+        if (lanes)                                                                              \
+            qsgd_dequant_lanes_kernel<P, NT>                                                    \
+                <<<grid, kBlockThreads, 0, stream>>>(norms, nibbles, n, d, dshift, s, out);     \
+        else                                                                                    \
+            qsgd_dequant_kernel<P, NT>                                                          \
+                <<<grid, kBlockThreads, 0, stream>>>(norms, nibbles, n, d, dshift, s, out);     \
+    } while (0)
     if (pow2) {
         if (tu.qsgd_dequant_nt)
             GCQ_DQ(true, true);

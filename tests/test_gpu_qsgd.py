@@ -142,6 +142,29 @@ def test_probability_zero_step_at_u_zero(gpu):
     assert np.all(out == 0.5)
 
 
+def test_dequant_paths_on_random_messages(gpu):
+    # qsgd_dequant takes a lane table (one quotient per lane, fetched across
+    # lanes) for d >= 341 and one division per element below: every nibble
+    # value (level 0 with either sign included) and special norms, bit-exact
+    # against the oracle's decode (NaN bits canonical), on both sides of the
+    # switch and with buckets that straddle wavefront tiles
+    rs = np.random.default_rng(300)
+    for d in (300, 339, 340, 341, 342, 512, 1000, 1024, 2048, 4096, 1 << 20):
+        for n in (d, 5 * d + 3, 2048 * 7 + 1, 100_000):
+            say("qsgd dequant d", d, "n", n)
+            nb, nw = oracle.num_buckets(n, d), oracle.nibble_words(n)
+            nib = rs.integers(0, 1 << 32, nw, dtype=np.uint64).astype(np.uint32)
+            norms = rs.uniform(0, 4, nb).astype(np.float32)
+            norms[rs.integers(0, nb, 3)] = np.array([np.nan, np.inf, 1e-40], np.float32)
+            for s in (1, 3, 7):
+                out = host(gpu.qsgd_dequant(dev(norms), dev(nib), n, d, s))
+                want = oracle.qsgd_dequant(norms, nib, n, d, s)
+                ob, wb = bits(out).copy(), bits(want).copy()
+                ob[np.isnan(out)] = 0x7FC00000
+                wb[np.isnan(want)] = 0x7FC00000
+                assert np.array_equal(ob, wb), (d, n, s)
+
+
 def test_fused_and_generic_paths(gpu):
     # d = 512 runs the register-resident fused kernel, d = 512 * 65 the
     # generic norm + level kernels; both must match the oracle
