@@ -44,7 +44,8 @@ class Tuning(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in (
         "gc2_unroll", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
         "dq_lds_stores", "dq_blocks_per_cu", "dq_fp4_decode", "qsgd_nt", "qsgd_rcp",
-        "qsgd_dequant_nt", "qsgd_blocks_per_cu", "qsgd_dequant_blocks_per_cu")]
+        "qsgd_dequant_nt", "qsgd_blocks_per_cu", "qsgd_dequant_blocks_per_cu",
+        "qsgd_buckets_per_wave")]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

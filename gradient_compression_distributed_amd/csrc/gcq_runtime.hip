@@ -44,11 +44,15 @@ void init_locked()
     g_tuning.dq_lds_stores = env_flag("GCQ_DQ_LDS_STORES", 1);
     g_tuning.dq_blocks_per_cu = env_count("GCQ_DQ_BLOCKS_PER_CU", 0);
     g_tuning.dq_fp4_decode = env_flag("GCQ_DQ_FP4_DECODE", 1);
-    g_tuning.qsgd_nt = env_flag("GCQ_QSGD_NT", 0);
+    g_tuning.qsgd_nt = env_flag("GCQ_QSGD_NT", 1);
     g_tuning.qsgd_rcp = env_flag("GCQ_QSGD_RCP", 1);
     g_tuning.qsgd_dequant_nt = env_flag("GCQ_QSGD_DEQUANT_NT", 1);
-    g_tuning.qsgd_blocks_per_cu = env_count("GCQ_QSGD_BLOCKS_PER_CU", 32);
+    g_tuning.qsgd_blocks_per_cu = env_count("GCQ_QSGD_BLOCKS_PER_CU", 0);
     g_tuning.qsgd_dequant_blocks_per_cu = env_count("GCQ_QSGD_DEQUANT_BLOCKS_PER_CU", 0);
+    g_tuning.qsgd_buckets_per_wave = env_int("GCQ_QSGD_BUCKETS_PER_WAVE", 0);
+    if (g_tuning.qsgd_buckets_per_wave != 1 && g_tuning.qsgd_buckets_per_wave != 2 &&
+        g_tuning.qsgd_buckets_per_wave != 4)
+        g_tuning.qsgd_buckets_per_wave = 0;
     g_init = true;
 }
 
@@ -70,7 +74,9 @@ bool tuning_valid(const gcq_tuning &t)
            flag_ok(t.dq_nt_loads) && flag_ok(t.dq_nt_stores) && flag_ok(t.dq_lds_stores) &&
            count_ok(t.dq_blocks_per_cu) && flag_ok(t.dq_fp4_decode) && flag_ok(t.qsgd_nt) &&
            flag_ok(t.qsgd_rcp) && flag_ok(t.qsgd_dequant_nt) && count_ok(t.qsgd_blocks_per_cu) &&
-           count_ok(t.qsgd_dequant_blocks_per_cu);
+           count_ok(t.qsgd_dequant_blocks_per_cu) &&
+           (t.qsgd_buckets_per_wave == 0 || t.qsgd_buckets_per_wave == 1 ||
+            t.qsgd_buckets_per_wave == 2 || t.qsgd_buckets_per_wave == 4);
 }
 
 void set_tuning(const gcq_tuning &t)

@@ -136,111 +136,136 @@ __device__ __forceinline__ float uniform_f(float x)
     return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
 
-__device__ __forceinline__ double wave_sum(double x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x += __shfl_xor(x, off, kWave);
-    return x;
-}
-
 // Max-norm scaling (QSGD summary, Knowl 8): the running maximum of |g| that
 // a NaN never enters (compare, then select), and its wave reduction (the
 // maximum is exact, so the order does not matter).
 __device__ __forceinline__ float max_in(float m, float a) { return a > m ? a : m; }
 
-__device__ __forceinline__ float wave_max(float x)
+// Sum, maximum and "any" over the G lanes of an aligned lane group (G a
+// power of two dividing the wavefront): butterflies that stay in the group.
+template <uint32_t G>
+__device__ __forceinline__ double group_sum(double x)
 {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    for (uint32_t off = G / 2; off > 0; off >>= 1)
+        x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+template <uint32_t G>
+__device__ __forceinline__ float group_max(float x)
+{
+#pragma unroll
+    for (uint32_t off = G / 2; off > 0; off >>= 1) {
         const float y = __shfl_xor(x, off, kWave);
         x = max_in(x, y);
     }
     return x;
 }
 
+template <uint32_t G>
+__device__ __forceinline__ bool group_any(bool p, uint32_t grp)
+{
+    const uint64_t m = __ballot(p);
+    if constexpr (G == kWave)
+        return m != 0;
+    else
+        return ((m >> (grp * G)) & ((1ull << G) - 1u)) != 0;
+}
+
 // Fused norm + levels + nibbles for buckets of D = 256*C elements held in
-// registers: one wavefront per bucket, lane L holds elements 256c + 4L .. +3
-// (dwordx4 loads, 1 KiB per wave instruction).  The sum of squares is
-// accumulated in float64 (each square exact), reduced across the wave by
-// butterfly shuffles, square-rooted in float64 and rounded once to float32;
-// the norm is then wave-uniform (a scalar register).  Nibble words: lane
-// pairs (2m, 2m+1) hold the two halves of word 32c + m of chunk c; one DPP
-// neighbour swap per two chunks lets even lanes store chunk c's words and
-// odd lanes chunk c+1's.
+// registers.  A wavefront owns H consecutive buckets at a time, one per
+// aligned group of G = 64/H lanes; lane l of a group holds elements
+// 4G r + 4l .. +3 of its bucket for r = 0 .. R-1, R = C H (dwordx4 loads,
+// 16 G contiguous bytes per group and instruction).  The sum of squares is
+// accumulated in float64 (each square exact), reduced across the group by
+// butterfly shuffles, square-rooted in float64 and rounded once to float32.
+// Everything a bucket costs beyond its elements (the reduction, the square
+// root, the reciprocal) is one instruction sequence for the H buckets
+// together, so H > 1 spreads it over more elements per lane.  Nibble words:
+// lane pairs (2m, 2m+1) of a group hold the two halves of word (G/2) r + m
+// of the bucket; one DPP neighbour swap per two chunks lets even lanes store
+// chunk r's words and odd lanes chunk r+1's.  In the last round a group past
+// the final bucket redoes that bucket and stores nothing.
 //
 // Max = true scales each bucket by its largest magnitude instead (Knowl 8).
 // A NaN does not enter that scale, so a bucket holding one takes the exact
 // level path (the division-free shortcut assumes finite inputs).
-template <int C, bool NT, bool Rcp, bool Max>
-__global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
+template <int C, int H, bool NT, bool Rcp, bool Max>
+__global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
     const float *__restrict__ g, uint32_t s, uint32_t k0, uint32_t k1, float *__restrict__ norms,
     uint32_t *__restrict__ nib, uint64_t nb_full)
 {
     constexpr uint64_t D = 256u * C;
+    constexpr uint32_t G = kWave / H;   // lanes per bucket
+    constexpr int R = C * H;            // float4 chunks per lane
+    constexpr uint32_t CH = 4u * G;     // elements per chunk
     const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t grp = lane / G, l = lane % G;
     const float sf = (float)s;
+    const uint64_t ngroups = (nb_full + H - 1) / H;
     const uint64_t wstride = (uint64_t)gridDim.x * kBlockWaves;
-    for (uint64_t b = (uint64_t)blockIdx.x * kBlockWaves + threadIdx.x / kWave; b < nb_full;
-         b += wstride) {
+    for (uint64_t bw = (uint64_t)blockIdx.x * kBlockWaves + threadIdx.x / kWave; bw < ngroups;
+         bw += wstride) {
+        const uint64_t braw = bw * H + grp;
+        const bool own = braw < nb_full;
+        const uint64_t b = own ? braw : nb_full - 1;
         const uint64_t base = b * D;
-        v4f v[C];
+        v4f v[R];
 #pragma unroll
-        for (int c = 0; c < C; ++c)
-            v[c] = ld<NT>(reinterpret_cast<const v4f *>(g + base + 256u * c) + lane);
-        // the draws do not depend on the norm: computing them first overlaps
-        // the Philox arithmetic with the latency of the wave reduction
-        float U[C][4];
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-            uniforms4_int((base + 256u * c + 4u * lane) >> 2, k0, k1, U[c]);
+        for (int r = 0; r < R; ++r)
+            v[r] = ld<NT>(reinterpret_cast<const v4f *>(g + base + CH * r) + l);
         float norm;
         bool finite_bucket = true;
         if constexpr (Max) {
             float m = 0.0f;
             bool nan = false;
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                m = max_in(m, fabsf(v[c].x));
-                m = max_in(m, fabsf(v[c].y));
-                m = max_in(m, fabsf(v[c].z));
-                m = max_in(m, fabsf(v[c].w));
-                nan = nan | (v[c].x != v[c].x) | (v[c].y != v[c].y) | (v[c].z != v[c].z) |
-                      (v[c].w != v[c].w);
+            for (int r = 0; r < R; ++r) {
+                m = max_in(m, fabsf(v[r].x));
+                m = max_in(m, fabsf(v[r].y));
+                m = max_in(m, fabsf(v[r].z));
+                m = max_in(m, fabsf(v[r].w));
+                nan = nan | (v[r].x != v[r].x) | (v[r].y != v[r].y) | (v[r].z != v[r].z) |
+                      (v[r].w != v[r].w);
             }
-            norm = uniform_f(wave_max(m));
-            finite_bucket = !__any(nan);
+            norm = group_max<G>(m);
+            finite_bucket = !group_any<G>(nan, grp);
         } else {
             double ss = 0.0;
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                ss = __builtin_fma((double)v[c].x, (double)v[c].x, ss);
-                ss = __builtin_fma((double)v[c].y, (double)v[c].y, ss);
-                ss = __builtin_fma((double)v[c].z, (double)v[c].z, ss);
-                ss = __builtin_fma((double)v[c].w, (double)v[c].w, ss);
+            for (int r = 0; r < R; ++r) {
+                ss = __builtin_fma((double)v[r].x, (double)v[r].x, ss);
+                ss = __builtin_fma((double)v[r].y, (double)v[r].y, ss);
+                ss = __builtin_fma((double)v[r].z, (double)v[r].z, ss);
+                ss = __builtin_fma((double)v[r].w, (double)v[r].w, ss);
             }
-            ss = wave_sum(ss);
-            norm = uniform_f((float)__builtin_sqrt(ss));
+            ss = group_sum<G>(ss);
+            norm = (float)__builtin_sqrt(ss);
         }
-        if (lane == 0)
+        if constexpr (H == 1)
+            norm = uniform_f(norm);   // wave-uniform: scalar registers from here on
+        if (own && l == 0)
             norms[b] = norm;
         const bool fast = Rcp && rcp_norm_ok(norm) && finite_bucket;
         const float rs = fast ? (1.0f / norm) * sf : 0.0f;
-        uint32_t h[C];
+        uint32_t h[R];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const float gq[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+        for (int r = 0; r < R; ++r) {
+            const float gq[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+            float U[4];
+            uniforms4_int((base + CH * r + 4u * l) >> 2, k0, k1, U);
             uint32_t lv[4];
             bool all_ok = false;
             if (fast) {
                 float dist[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[c][q], dist[q]);
+                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[q], dist[q]);
                 all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
             }
             if (all_ok) {
-                h[c] = pack4(gq, lv);
+                h[r] = pack4(gq, lv);
             } else {
                 // rare: redo the group element by element, the exact way
                 // where the shortcut cannot decide
@@ -248,27 +273,29 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_fused_kernel(
                 for (int q = 0; q < 4; ++q) {
                     float dist = 1.0f;
                     if (fast)
-                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[c][q], dist);
+                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[q], dist);
                     if (!(dist < kSafeDist))
-                        lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, U[c][q] * 0x1p-24f);
+                        lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, U[q] * 0x1p-24f);
                 }
-                h[c] = pack4_exact(gq, lv);
+                h[r] = pack4_exact(gq, lv);
             }
         }
-        uint32_t *out = nib + (base >> 3);
+        uint32_t *out = nib + (base >> 3) + (l >> 1);
         const bool odd = (lane & 1u) != 0;
 #pragma unroll
-        for (int c = 0; c < C; c += 2) {
-            if (c + 1 < C) {
-                const uint32_t y = dev::dpp<dev::kSwapPairs>(odd ? h[c] : h[c + 1]);
-                if (odd)
-                    st<NT>(out + 32u * (c + 1) + (lane >> 1), (y << 16) | h[c + 1]);
-                else
-                    st<NT>(out + 32u * c + (lane >> 1), (h[c] << 16) | y);
+        for (int r = 0; r < R; r += 2) {
+            if (r + 1 < R) {
+                const uint32_t y = dev::dpp<dev::kSwapPairs>(odd ? h[r] : h[r + 1]);
+                if (own) {
+                    if (odd)
+                        st<NT>(out + (G / 2u) * (r + 1), (y << 16) | h[r + 1]);
+                    else
+                        st<NT>(out + (G / 2u) * r, (h[r] << 16) | y);
+                }
             } else {
-                const uint32_t y = dev::dpp<dev::kSwapPairs>(h[c]);
-                if (!odd)
-                    st<NT>(out + 32u * c + (lane >> 1), (h[c] << 16) | y);
+                const uint32_t y = dev::dpp<dev::kSwapPairs>(h[r]);
+                if (own && !odd)
+                    st<NT>(out + (G / 2u) * r, (h[r] << 16) | y);
             }
         }
     }
@@ -315,14 +342,14 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_wave_kernel(
             float m = 0.0f;
             for (uint64_t e = lo + lane; e < hi; e += kWave)
                 m = max_in(m, fabsf(g[e]));
-            m = wave_max(m);
+            m = group_max<kWave>(m);
             if (lane == 0)
                 norms[b] = m;
         } else {
             double ss = 0.0;
             for (uint64_t e = lo + lane; e < hi; e += kWave)
                 ss = __builtin_fma((double)g[e], (double)g[e], ss);
-            ss = wave_sum(ss);
+            ss = group_sum<kWave>(ss);
             if (lane == 0)
                 norms[b] = (float)__builtin_sqrt(ss);
         }
@@ -700,36 +727,57 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_generic_kernel(
     }
 }
 
-template <int CC, bool Max>
-void launch_fused(const gcq_tuning &tu, uint32_t grid, const float *g, uint32_t s, uint32_t k0,
-                  uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
-                  hipStream_t stream)
+template <int CC, int H, bool Max>
+void launch_fused(const gcq_tuning &tu, const float *g, uint32_t s, uint32_t k0, uint32_t k1,
+                  float *norms, uint32_t *nibbles, uint64_t nb_done, hipStream_t stream)
 {
+    const uint64_t waves = (nb_done + H - 1) / H;
+    const uint32_t grid = grid_for((waves + kBlockWaves - 1) / kBlockWaves, tu.qsgd_blocks_per_cu);
     if (tu.qsgd_nt && tu.qsgd_rcp)
-        qsgd_fused_kernel<CC, true, true, Max>
+        qsgd_fused_kernel<CC, H, true, true, Max>
             <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
     else if (tu.qsgd_nt)
-        qsgd_fused_kernel<CC, true, false, Max>
+        qsgd_fused_kernel<CC, H, true, false, Max>
             <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
     else if (tu.qsgd_rcp)
-        qsgd_fused_kernel<CC, false, true, Max>
+        qsgd_fused_kernel<CC, H, false, true, Max>
             <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
     else
-        qsgd_fused_kernel<CC, false, false, Max>
+        qsgd_fused_kernel<CC, H, false, false, Max>
             <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
 }
 
+// Buckets per wavefront: the knob (0: as many as make 4 float4 chunks per
+// lane, which measured fastest), limited to C H <= 4 chunks per lane
+// (register budget).
 template <bool Max>
-void launch_fused_c(uint32_t C, const gcq_tuning &tu, uint32_t grid, const float *g, uint32_t s,
-                    uint32_t k0, uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
+void launch_fused_c(uint32_t C, const gcq_tuning &tu, const float *g, uint32_t s, uint32_t k0,
+                    uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
                     hipStream_t stream)
 {
+    const uint32_t hmax = C <= 4 ? 4u / C : 1u;
+    const uint32_t want = tu.qsgd_buckets_per_wave ? (uint32_t)tu.qsgd_buckets_per_wave : hmax;
+    const uint32_t H = want < hmax ? want : hmax;
+#define GCQ_F(CC, HH) launch_fused<CC, HH, Max>(tu, g, s, k0, k1, norms, nibbles, nb_done, stream)
     switch (C) {
-    case 1: launch_fused<1, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
-    case 2: launch_fused<2, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
-    case 4: launch_fused<4, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
-    default: launch_fused<8, Max>(tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream); break;
+    case 1:
+        if (H >= 4)
+            GCQ_F(1, 4);
+        else if (H == 2)
+            GCQ_F(1, 2);
+        else
+            GCQ_F(1, 1);
+        break;
+    case 2:
+        if (H >= 2)
+            GCQ_F(2, 2);
+        else
+            GCQ_F(2, 1);
+        break;
+    case 4: GCQ_F(4, 1); break;
+    default: GCQ_F(8, 1); break;
     }
+#undef GCQ_F
 }
 
 }  // namespace
@@ -748,12 +796,10 @@ hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t
     if (C == 1 || C == 2 || C == 4 || C == 8) {
         nb_done = n / d;
         if (nb_done) {
-            const uint32_t grid =
-                grid_for((nb_done + kBlockWaves - 1) / kBlockWaves, tu.qsgd_blocks_per_cu);
-if (maxnorm)
-                launch_fused_c<true>(C, tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream);
+            if (maxnorm)
+                launch_fused_c<true>(C, tu, g, s, k0, k1, norms, nibbles, nb_done, stream);
             else
-                launch_fused_c<false>(C, tu, grid, g, s, k0, k1, norms, nibbles, nb_done, stream);
+                launch_fused_c<false>(C, tu, g, s, k0, k1, norms, nibbles, nb_done, stream);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;

@@ -431,7 +431,8 @@ typedef struct gcq_tuning {
     int dq_fp4_decode;     /* 1: decode two codes per instruction with the FP4
                               conversion (default); 0: one signed-byte
                               conversion per code */
-    int qsgd_nt;           /* 1: non-temporal hints in the QSGD quantizer */
+    int qsgd_nt;           /* 1: non-temporal hints in the QSGD quantizer
+                              (default) */
     int qsgd_rcp;          /* 1: division-free level arithmetic in the QSGD
                               quantizer that provably reproduces the results of
                               the per-element IEEE division, with an exact
@@ -439,12 +440,16 @@ typedef struct gcq_tuning {
                               division per element */
     int qsgd_dequant_nt;   /* 1: non-temporal hints in qsgd_dequant */
     int qsgd_blocks_per_cu; /* fused QSGD quantizer (d a multiple of 256, up to
-                               2048): 0: one wavefront per bucket; k > 0: k
-                               workgroups per compute unit, each wavefront
-                               strides over many buckets (default 32) */
+                               2048): 0: one wavefront per group of buckets
+                               (default); k > 0: k workgroups per compute
+                               unit, each wavefront strides over many groups */
     int qsgd_dequant_blocks_per_cu; /* qsgd_dequant: 0: one wavefront per
                                1024 elements; k > 0: k workgroups per compute
                                unit, grid-stride (default 0) */
+    int qsgd_buckets_per_wave; /* fused QSGD quantizer: buckets H a
+                               wavefront takes at once, one per group of 64/H
+                               lanes: 1, 2 or 4, limited to d H <= 1024; 0:
+                               H = 1024/d for d <= 1024, else 1 (default) */
 } gcq_tuning;
 
 /*

@@ -142,6 +142,37 @@ def test_probability_zero_step_at_u_zero(gpu):
     assert np.all(out == 0.5)
 
 
+@pytest.mark.parametrize("h", [0, 1, 2, 4])
+def test_buckets_per_wave(knobs, h):
+    # the fused quantizer with 1, 2 or 4 buckets per wavefront (lane groups
+    # of 64, 32 or 16; 0 picks by d), each with one wavefront per group and
+    # with wavefronts striding over groups: bucket counts that leave the last group of a
+    # wavefront without a bucket, ragged tails, NaN / Inf / zero buckets, the
+    # L2 and the max-norm scales
+    gpu = knobs
+    rs = np.random.default_rng(400 + h)
+    for d in (256, 512, 1024, 2048):
+        for nbk in (1, 2, 3, 5, 6, 7, 33):
+            gpu.set_tuning(qsgd_buckets_per_wave=h, qsgd_blocks_per_cu=(0 if nbk % 2 else 1))
+            n = nbk * d + (int(rs.integers(1, d)) if nbk % 2 else 0)
+            say("qsgd buckets/wave", h, "d", d, "n", n)
+            g = wl.qsgd_spiky(n, d, int(rs.integers(1 << 30)))
+            if nbk >= 5:
+                g[d + 3] = np.nan
+                g[2 * d:3 * d] = 0.0
+                g[3 * d + 1] = -np.inf
+            seed = int(rs.integers(1 << 62))
+            s = int(rs.choice([1, 3, 7]))
+            check_case(gpu, g, d, s, seed)
+            sc_d, nib_d = gpu.qsgd_quantize_maxnorm(dev(g), d, s, seed)
+            sc_h, nib_h = oracle.qsgd_quantize_maxnorm(g, d, s, seed)
+            sc = host(sc_d)
+            assert np.array_equal(np.isnan(sc), np.isnan(sc_h))
+            ok = ~np.isnan(sc_h)
+            assert np.array_equal(bits(sc[ok]), bits(sc_h[ok])), (h, d, n)
+            assert np.array_equal(host(nib_d), nib_h), (h, d, n)
+
+
 def test_dequant_paths_on_random_messages(gpu):
     # qsgd_dequant takes a lane table (one quotient per lane, fetched across
     # lanes) for d >= 341 and one division per element below: every nibble
