@@ -11,17 +11,24 @@
 // significant first in 32-bit words; bit_offsets[b] is where bucket b starts
 // and bit_offsets[nb] the total length.
 //
-// Encode, one wavefront per bucket (d a multiple of 8, at most 2048):
-//   lengths -- per chunk of 64 coordinates, a ballot of the non-zero ones
-//              gives each its predecessor and code length; the bucket's
-//              length goes to the offsets array, then an exclusive scan;
+// Encode (d a multiple of 8, at most 2048), one wavefront per bucket, four
+// per workgroup, steps of 512 coordinates (lane L takes nibble word L):
+//   lengths -- each lane walks the non-zero nibbles of its word, its first
+//              predecessor taken from the nearest lower lane with one (a
+//              ballot and a shuffle); the wavefront sums the code lengths
+//              into the offsets array, then an exclusive scan;
 //   zero    -- each bucket that starts inside a word clears that word (it is
 //              shared with the previous bucket);
-//   write   -- the wavefront assembles its bucket's bits in LDS (LDS atomic
-//              ORs at the scanned positions) and writes the words out: plain
-//              stores, atomic ORs for the two words it may share.
-// Decode is sequential per bucket (variable-length codes): one thread per
-// bucket, every read checked against the bucket's end.
+//   write   -- the non-zero coordinates of a step are compacted into an LDS
+//              list (a wavefront scan of the lanes' counts), then coded 64 at
+//              a time, one per lane, at positions from a second scan; codes
+//              are ORed into the bucket's bits in LDS, which leave as plain
+//              stores (atomic ORs for the two words a bucket may share).
+// Decode: one lane per bucket (variable-length codes are read in order), a
+// wavefront per 64 consecutive buckets.  Their bits, one contiguous range,
+// are first copied into LDS with coalesced loads; each coordinate is then
+// parsed from a 64-bit register window.  Every read stays inside the
+// bucket and the input.
 #include "gcq_device.h"
 #include "gcq_internal.h"
 
@@ -32,21 +39,6 @@ namespace {
 __device__ __host__ __forceinline__ uint32_t bit_length(uint32_t k)
 {
     return k ? 32u - (uint32_t)__builtin_clz(k) : 0u;
-}
-
-// omega(k) as a right-aligned bit string and its length (k >= 1, at most 32
-// bits for the values here: distances up to 2048, levels up to 7).
-__device__ __forceinline__ uint32_t omega_code(uint32_t k, uint32_t &len)
-{
-    uint64_t code = 0;   // the final 0
-    len = 1;
-    while (k > 1) {
-        const uint32_t b = bit_length(k);
-        code |= (uint64_t)k << len;
-        len += b;
-        k = b - 1;
-    }
-    return (uint32_t)code;
 }
 
 __device__ __host__ __forceinline__ uint32_t omega_length(uint32_t k)
@@ -60,63 +52,166 @@ __device__ __host__ __forceinline__ uint32_t omega_length(uint32_t k)
     return len;
 }
 
-// The per-coordinate step shared by both encode passes: for coordinate li of
-// the bucket (one per lane in this chunk), its nibble, whether it is coded,
-// its code length, and the exclusive bit position within the bucket's codes.
-struct Coord {
-    uint32_t nib, len, code_d, len_d;
-    uint64_t pos;
-};
+// omega lengths L(k) = b + L(b - 1), b the bit length of k, L(0) = 0: for
+// k <= 11 the table below (4 bits per entry, entry k at bit 4k), so for
+// 1 <= k <= 4095 one lookup after the bit length.
+constexpr uint64_t kOmegaLenTable = 0x777766663310ull;
 
-__device__ __forceinline__ Coord coord_step(const uint32_t *__restrict__ nibbles, uint64_t lo,
-                                            uint32_t li, uint32_t bucket_len, uint32_t lane,
-                                            int32_t &prev, uint64_t &bits)
+__device__ __forceinline__ uint32_t omega_len_small(uint32_t k)   // 0 <= k <= 11
 {
-    Coord c;
-    c.nib = 0;
-    if (li < bucket_len) {
-        const uint64_t i = lo + li;
-        c.nib = (nibbles[i >> 3] >> (28u - 4u * (uint32_t)(i & 7u))) & 15u;
-    }
-    const bool nz = (c.nib & 7u) != 0u;
-    const uint64_t mask = __ballot(nz);
-    const uint64_t below = mask & ((1ull << lane) - 1ull);
-    const int32_t chunk0 = (int32_t)(li - lane);
-    const int32_t p = below ? chunk0 + 63 - (int32_t)__builtin_clzll(below) : prev;
-    c.code_d = 0;
-    c.len_d = 0;
-    c.len = 0;
-    if (nz) {
-        c.code_d = omega_code((uint32_t)((int32_t)li - p), c.len_d);
-        c.len = c.len_d + 1u + omega_length(c.nib & 7u);
-    }
-    // exclusive scan of the lengths across the wavefront
-    uint32_t incl = c.len;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off, kWave);
-        if (lane >= (uint32_t)off)
-            incl += y;
-    }
-    c.pos = bits + incl - c.len;
-    bits += __shfl(incl, kWave - 1, kWave);
-    if (mask)
-        prev = chunk0 + 63 - (int32_t)__builtin_clzll(mask);
-    return c;
+    return (uint32_t)(kOmegaLenTable >> (4u * k)) & 15u;
 }
 
-__global__ __launch_bounds__(kWave) void elias_length_kernel(const uint32_t *__restrict__ nibbles,
-                                                              uint64_t n, uint32_t d, uint64_t nb,
-                                                              uint64_t *__restrict__ offs)
+__device__ __forceinline__ uint32_t omega_len_fast(uint32_t k)   // 1 <= k <= 4095
 {
-    const uint32_t lane = threadIdx.x;
-    for (uint64_t b = blockIdx.x; b < nb; b += gridDim.x) {
+    const uint32_t b = 32u - (uint32_t)__builtin_clz(k);
+    return b + omega_len_small(b - 1u);
+}
+
+// omega(k) right-aligned, 1 <= k <= 4095: at most three groups (the binary
+// digits of k, of its bit length - 1, ...), the last one found first in the
+// code, then the final 0.
+__device__ __forceinline__ uint32_t omega_code_fast(uint32_t k, uint32_t &len)
+{
+    uint32_t code = 0, n = 1;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        if (k > 1u) {
+            const uint32_t b = 32u - (uint32_t)__builtin_clz(k);
+            code |= k << n;
+            n += b;
+            k = b - 1u;
+        }
+    }
+    len = n;
+    return code;
+}
+
+// Per nibble word: bit 4k set when nibble k (from the least significant
+// end) has a non-zero level.  Coordinate j of the word is nibble 7 - j: its
+// level in bits 28 - 4j .. 30 - 4j, its sign in bit 31 - 4j.
+__device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w)
+{
+    return (w | (w >> 1) | (w >> 2)) & 0x11111111u;
+}
+
+// The lane's nibble word of the step starting at coordinate c0, with the
+// coordinates at or past the bucket's length cleared.
+__device__ __forceinline__ uint32_t step_word(const uint32_t *__restrict__ nibbles, uint64_t lo,
+                                              uint32_t li0, uint32_t blen)
+{
+    if (li0 >= blen)
+        return 0u;
+    uint32_t w = nibbles[(lo + li0) >> 3];
+    if (li0 + 8u > blen)
+        w &= ~0u << (4u * (li0 + 8u - blen));
+    return w;
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, uint32_t lane)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, kWave);
+        if (lane >= (uint32_t)off)
+            x += y;
+    }
+    return x;
+}
+
+constexpr uint32_t kEliasStep = 8u * kWave;   // coordinates per wavefront step
+
+// Coded coordinates of a nibble word as an 8-bit mask, coordinate j of the
+// word in bit 7 - j (so the previous coordinate is one bit higher).
+__device__ __forceinline__ uint32_t coord_mask8(uint32_t w)
+{
+    uint32_t m = nonzero_nibbles(w);       // bit 4k: nibble k from the least significant
+    m = (m | (m >> 3)) & 0x03030303u;
+    m = (m | (m >> 6)) & 0x000F000Fu;
+    return (m | (m >> 12)) & 0xFFu;
+}
+
+// Code bits of a nibble word's coordinates except the omega code of its
+// first coordinate's distance (which depends on earlier words):
+//   sign + omega(level): 1 + L(level) = 2, 4 or 7 bits for levels 1, 2-3,
+//   4-7, counted with popcounts of the level bits;
+//   omega(gap) for each later coordinate of the word, gap <= 7: L = 1, 3 or
+//   6, i.e. 1 + 2 [gap >= 2] + 3 [gap >= 4], where gap >= 2 means the
+//   coordinate just before is not coded, gap >= 4 the three before.
+__device__ __forceinline__ uint32_t word_code_bits(uint32_t w, uint32_t m8)
+{
+    const uint32_t nz = nonzero_nibbles(w);
+    const uint32_t ge2 = ((w >> 1) | (w >> 2)) & 0x11111111u;
+    const uint32_t ge4 = (w >> 2) & 0x11111111u;
+    uint32_t bits = 2u * (uint32_t)__builtin_popcount(nz) + 2u * (uint32_t)__builtin_popcount(ge2) +
+                    3u * (uint32_t)__builtin_popcount(ge4);
+    const uint32_t rest = m8 ? m8 & ~(0x80000000u >> (uint32_t)__builtin_clz(m8)) : 0u;
+    const uint32_t gap2 = rest & ~(m8 >> 1);
+    const uint32_t gap4 = gap2 & ~(m8 >> 2) & ~(m8 >> 3);
+    bits += (uint32_t)__builtin_popcount(rest) + 2u * (uint32_t)__builtin_popcount(gap2) +
+            3u * (uint32_t)__builtin_popcount(gap4);
+    return bits;
+}
+
+// The bits of one step's nibble word (lane-local), with the predecessor of
+// its first coded coordinate taken from the nearest lower lane that has one,
+// or from earlier steps (prev); prev moves to the step's last coded one.
+struct StepWord {
+    uint32_t w, m8, bits;
+    int32_t pred;   // coordinate before the word's first coded one (-1: none)
+};
+
+__device__ __forceinline__ StepWord step_bits(uint32_t w, uint32_t li0, uint32_t lane,
+                                              int32_t &prev)
+{
+    StepWord sw;
+    sw.w = w;
+    sw.m8 = coord_mask8(w);
+    const int32_t first = (int32_t)(li0 + (uint32_t)__builtin_clz(sw.m8 | 1u) - 24u);
+    const int32_t last = sw.m8 ? (int32_t)(li0 + 7u - (uint32_t)__builtin_ctz(sw.m8)) : -1;
+    const uint64_t any = __ballot(sw.m8 != 0u);
+    const uint64_t below = any & ((1ull << lane) - 1ull);
+    const int32_t from_below = __shfl(last, below ? 63 - (int)__builtin_clzll(below) : 0, kWave);
+    sw.pred = below ? from_below : prev;
+    sw.bits = sw.m8 ? word_code_bits(w, sw.m8) + omega_len_fast((uint32_t)(first - sw.pred)) : 0u;
+    if (any)
+        prev = __shfl(last, 63 - (int)__builtin_clzll(any), kWave);
+    return sw;
+}
+
+constexpr int kEliasBlocksPerCU = 8;   // grid-stride workgroups per compute unit
+
+__global__ __launch_bounds__(kBlockThreads) void elias_length_kernel(
+    const uint32_t *__restrict__ nibbles, uint64_t n, uint32_t d, uint64_t nb,
+    uint64_t *__restrict__ offs)
+{
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint64_t wstride = (uint64_t)gridDim.x * kBlockWaves;
+    uint64_t b = (uint64_t)blockIdx.x * kBlockWaves + threadIdx.x / kWave;
+    // the first word of the next bucket is loaded one bucket ahead
+    uint32_t w_next = 0;
+    if (b < nb) {
+        const uint64_t lo = b * d;
+        w_next = step_word(nibbles, lo, 8u * lane, (uint32_t)(lo + d < n ? d : n - lo));
+    }
+    for (; b < nb; b += wstride) {
         const uint64_t lo = b * d;
         const uint32_t blen = (uint32_t)(lo + d < n ? d : n - lo);
+        const uint32_t w0 = w_next;
+        if (b + wstride < nb) {
+            const uint64_t lo2 = (b + wstride) * d;
+            w_next = step_word(nibbles, lo2, 8u * lane, (uint32_t)(lo2 + d < n ? d : n - lo2));
+        }
         int32_t prev = -1;
-        uint64_t bits = 0;
-        for (uint32_t c0 = 0; c0 < blen; c0 += kWave)
-            (void)coord_step(nibbles, lo, c0 + lane, blen, lane, prev, bits);
+        uint32_t bits = 0;
+        for (uint32_t c0 = 0; c0 < blen; c0 += kEliasStep) {
+            const uint32_t li0 = c0 + 8u * lane;
+            const uint32_t w = c0 ? step_word(nibbles, lo, li0, blen) : w0;
+            bits += step_bits(w, li0, lane, prev).bits;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            bits += __shfl_xor(bits, off, kWave);
         if (lane == 0)
             offs[b] = 32u + bits;
     }
@@ -135,82 +230,151 @@ __global__ __launch_bounds__(kBlockThreads) void elias_zero_kernel(const uint64_
     }
 }
 
-__global__ __launch_bounds__(kWave) void elias_write_kernel(const float *__restrict__ norms,
-                                                             const uint32_t *__restrict__ nibbles,
-                                                             uint64_t n, uint32_t d, uint64_t nb,
-                                                             const uint64_t *__restrict__ offs,
-                                                             uint32_t *__restrict__ out,
-                                                             uint64_t cap, uint32_t lds_words)
+// LDS: the omega codes of 1..d ((length << 24) | code, one word each,
+// shared by the workgroup), then per wavefront the bucket's bits
+// (region_words words: the start's shift, the norm, every coordinate at its
+// longest code, and the word a code may spill into).  Each lane codes the
+// coordinates of its nibble word at the position a wavefront scan of the
+// lanes' code lengths gives it; a bucket's offsets, inputs and first words
+// are loaded one group ahead.
+struct WriteFetch {
+    uint64_t start, end;
+    uint32_t norm_bits, w0;
+};
+
+__device__ __forceinline__ WriteFetch write_fetch(const float *__restrict__ norms,
+                                                  const uint32_t *__restrict__ nibbles,
+                                                  const uint64_t *__restrict__ offs, uint64_t n,
+                                                  uint32_t d, uint64_t nb, uint64_t b,
+                                                  uint32_t lane)
 {
-    extern __shared__ uint32_t bucket_bits[];
-    const uint32_t lane = threadIdx.x;
-    for (uint64_t b = blockIdx.x; b < nb; b += gridDim.x) {
+    WriteFetch f{0u, 0u, 0u, 0u};
+    if (b < nb) {
         const uint64_t lo = b * d;
-        const uint32_t blen = (uint32_t)(lo + d < n ? d : n - lo);
-        const uint64_t start = offs[b], end = offs[b + 1];
-        const uint32_t sh = (uint32_t)(start & 31u);
-        for (uint32_t k = lane; k < lds_words; k += kWave)
-            bucket_bits[k] = 0u;
-        __syncthreads();
-        if (lane == 0) {
-            const uint64_t v = (uint64_t)__float_as_uint(norms[b]) << (32u - sh);
-            atomicOr(&bucket_bits[0], (uint32_t)(v >> 32));
-            atomicOr(&bucket_bits[1], (uint32_t)v);
+        f.start = offs[b];
+        f.end = offs[b + 1];
+        f.norm_bits = __float_as_uint(norms[b]);
+        f.w0 = step_word(nibbles, lo, 8u * lane, (uint32_t)(lo + d < n ? d : n - lo));
+    }
+    return f;
+}
+
+__global__ __launch_bounds__(kBlockThreads) void elias_write_kernel(
+    const float *__restrict__ norms, const uint32_t *__restrict__ nibbles, uint64_t n, uint32_t d,
+    uint64_t nb, const uint64_t *__restrict__ offs, uint32_t *__restrict__ out, uint64_t cap,
+    uint32_t region_words)
+{
+    extern __shared__ uint32_t elias_lds[];
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t *codes = elias_lds;
+    uint32_t *bits = elias_lds + (d + 1u) + wave * region_words;
+    for (uint32_t k = threadIdx.x + 1u; k <= d; k += kBlockThreads) {
+        uint32_t len;
+        const uint32_t c = omega_code_fast(k, len);
+        codes[k] = (len << 24) | c;
+    }
+    const uint64_t ngroups = (nb + kBlockWaves - 1) / kBlockWaves;
+    uint64_t grp = blockIdx.x;
+    WriteFetch next = write_fetch(norms, nibbles, offs, n, d, nb, grp * kBlockWaves + wave, lane);
+    for (; grp < ngroups; grp += gridDim.x) {
+        const uint64_t b = grp * kBlockWaves + wave;
+        const bool valid = b < nb;
+        const WriteFetch cur = next;
+        if (grp + gridDim.x < ngroups)
+            next = write_fetch(norms, nibbles, offs, n, d, nb, (grp + gridDim.x) * kBlockWaves + wave,
+                               lane);
+        const uint64_t lo = b * d;
+        const uint32_t blen = valid ? (uint32_t)(lo + d < n ? d : n - lo) : 0u;
+        const uint32_t sh = (uint32_t)(cur.start & 31u);
+        uint64_t nwl = valid ? ((uint64_t)sh + (cur.end - cur.start) + 31u) / 32u + 1u : 0u;
+        nwl = nwl < region_words ? nwl : region_words;
+        for (uint32_t k = lane; k < nwl; k += kWave)
+            bits[k] = 0u;
+        __syncthreads();   // the cleared bits (and, the first time, the code table)
+        if (valid && lane == 0) {
+            const uint64_t v = (uint64_t)cur.norm_bits << (32u - sh);
+            atomicOr(&bits[0], (uint32_t)(v >> 32));
+            atomicOr(&bits[1], (uint32_t)v);
         }
         int32_t prev = -1;
-        uint64_t bits = 0;
-        for (uint32_t c0 = 0; c0 < blen; c0 += kWave) {
-            const Coord c = coord_step(nibbles, lo, c0 + lane, blen, lane, prev, bits);
-            if (c.len) {
-                // code = omega(dist) | sign | omega(level), c.len <= 26 bits
-                uint32_t len_l;
-                const uint32_t code_l = omega_code(c.nib & 7u, len_l);
-                const uint64_t code = ((((uint64_t)c.code_d << 1) | (c.nib >> 3)) << len_l) | code_l;
-                const uint64_t p = (uint64_t)sh + 32u + c.pos;     // < lds_words * 32
-                const uint32_t w = (uint32_t)(p >> 5), o = (uint32_t)(p & 31u);
-                const uint64_t v = code << (64u - c.len - o);
-                atomicOr(&bucket_bits[w], (uint32_t)(v >> 32));
-                if ((uint32_t)v)
-                    atomicOr(&bucket_bits[w + 1], (uint32_t)v);
+        uint32_t pos = sh + 32u;   // region bit position of the step's first code
+        for (uint32_t c0 = 0; c0 < blen; c0 += kEliasStep) {
+            const uint32_t li0 = c0 + 8u * lane;
+            const StepWord sw =
+                step_bits(c0 ? step_word(nibbles, lo, li0, blen) : cur.w0, li0, lane, prev);
+            const uint32_t incl = wave_inclusive_scan(sw.bits, lane);
+            uint32_t q = pos + incl - sw.bits;
+            pos += __shfl(incl, kWave - 1, kWave);
+            uint32_t m = sw.m8;
+            int32_t p = sw.pred;
+            while (m) {
+                const uint32_t h = 31u - (uint32_t)__builtin_clz(m);   // coordinate 7 - h
+                const uint32_t idx = li0 + 7u - h;
+                const uint32_t nibv = (sw.w >> (4u * h)) & 15u;
+                const uint32_t cd = codes[(uint32_t)((int32_t)idx - p)];
+                const uint32_t cl = codes[nibv & 7u];
+                const uint32_t llen = cl >> 24;
+                const uint32_t code =
+                    ((((cd & 0xFFFFFFu) << 1) | (nibv >> 3)) << llen) | (cl & 0xFFFFFFu);
+                const uint32_t len = (cd >> 24) + 1u + llen;   // <= 26 bits
+                // q + len stays inside the bucket's region by construction (the
+                // lengths are the ones that made the offsets); checked anyway
+                const uint32_t wd = q >> 5, o = q & 31u;
+                if (wd + 1u < region_words) {
+                    const uint64_t v = (uint64_t)code << (64u - len - o);
+                    atomicOr(&bits[wd], (uint32_t)(v >> 32));
+                    if ((uint32_t)v)
+                        atomicOr(&bits[wd + 1], (uint32_t)v);
+                }
+                q += len;
+                p = (int32_t)idx;
+                m &= ~(1u << h);
             }
         }
-        __syncthreads();
-        const uint64_t nw = (sh + (end - start) + 31u) >> 5;
-        const bool shares_last = ((end & 31u) != 0u) && (b + 1 < nb);
+        __syncthreads();   // every code is in
+        const uint64_t nw = valid ? ((uint64_t)sh + (cur.end - cur.start) + 31u) >> 5 : 0u;
+        const bool shares_last = ((cur.end & 31u) != 0u) && (b + 1 < nb);
         for (uint64_t k = lane; k < nw; k += kWave) {
-            const uint64_t gw = (start >> 5) + k;
+            const uint64_t gw = (cur.start >> 5) + k;
             if (gw >= cap)
                 continue;
-            const uint32_t v = bucket_bits[k];
+            const uint32_t v = bits[k];
             if ((k == 0 && sh) || (k == nw - 1 && shares_last))
                 atomicOr(&out[gw], v);
             else
                 out[gw] = v;
         }
-        __syncthreads();
+        __syncthreads();   // the bits are cleared for the next group
     }
 }
 
-// Sequential decode of one bucket per thread.  The bits stream through a
-// 64-bit register window refilled a word at a time (one load per 32 bits
-// consumed); the bucket's nibble words are built in a register and stored
-// once each.  Nothing past the bucket's end or the input is read; a code
-// that would run past the end stops the bucket (it then keeps the
-// coordinates decoded so far).
+// Decode.  A reader over one bucket's bits: a 64-bit window (next bit in
+// bit 63) refilled one word at a time from `src` (the staged copy in LDS, or
+// the input).  `left` counts the bucket's bits not yet consumed; it is
+// capped at 2^31, more than any bucket can consume before it stops (every
+// coordinate advances the index, and the reader fails on any omega group
+// of 31 or more digits).
+template <typename Src>
 struct BitReader {
-    const uint32_t *in;
-    uint64_t word;        // next word to load
-    uint64_t left;        // bits of the bucket not yet consumed
-    uint64_t buf;         // window, next bit in bit 63
+    Src src;              // the bucket's first word
+    uint32_t word;        // next word to load, relative to src
+    uint32_t left;
+    uint64_t buf;         // window
     uint32_t avail;       // valid bits in the window
     bool ok;
 
     __device__ void refill()
     {
-        while (avail <= 32u && (uint64_t)avail < left) {
-            buf |= (uint64_t)in[word++] << (32u - avail);
+        while (avail <= 32u && avail < left) {
+            buf |= (uint64_t)src[word++] << (32u - avail);
             avail += 32u;
         }
+    }
+    __device__ void consume(uint32_t nbits)
+    {
+        buf <<= nbits;
+        avail -= nbits;
+        left -= nbits;
     }
     __device__ uint32_t get(uint32_t nbits)   // 1..32 bits
     {
@@ -220,9 +384,7 @@ struct BitReader {
         }
         refill();
         const uint32_t v = (uint32_t)(buf >> (64u - nbits));
-        buf <<= nbits;
-        avail -= nbits;
-        left -= nbits;
+        consume(nbits);
         return v;
     }
     __device__ uint32_t omega()
@@ -239,52 +401,215 @@ struct BitReader {
     }
 };
 
+// One coordinate from the top 32 bits x of the window (next bit in bit 31):
+// omega(dist) with at most 3 groups, the sign, omega(level) with at most 2
+// groups, all read with shifts and selects (no branches).  An omega code is
+// groups, each a 1 and k more digits making the next k, ended by a 0; the
+// first group starts from k = 1.  Returns the code's length, or 0 when it
+// needs more groups (more than 31 bits); the caller checks it against the
+// bits the window holds.
+__device__ __forceinline__ uint32_t coord_peek(uint32_t x, uint32_t &dist, uint32_t &sign,
+                                               uint32_t &level)
+{
+    // omega(dist): continuation bits c0..c3, group values k1 (2 bits), k2
+    // (k1 + 1 bits), k3 (k2 + 1 bits)
+    const uint32_t c0 = x >> 31;
+    const uint32_t k1 = 2u | ((x >> 30) & 1u);
+    const uint32_t c1 = (x >> 29) & 1u;
+    const uint32_t k2 = (x << 2) >> (31u - k1);                  // k1 <= 3
+    const uint32_t c2 = (x << (3u + k1)) >> 31;
+    const uint32_t k3 = (x << (3u + k1)) >> (31u - k2);          // k2 <= 15
+    const uint32_t c3 = (x << (4u + k1 + k2)) >> 31;
+    const bool dok = !c0 || !c1 || !c2 || !c3;
+    dist = !c0 ? 1u : !c1 ? k1 : !c2 ? k2 : k3;
+    const uint32_t dlen = !c0 ? 1u : !c1 ? 3u : !c2 ? 4u + k1 : 5u + k1 + k2;   // <= 23
+    sign = (x << dlen) >> 31;
+    const uint32_t y = x << (dlen + 1u);
+    const uint32_t l0 = y >> 31;
+    const uint32_t m1 = 2u | ((y >> 30) & 1u);
+    const uint32_t l1 = (y >> 29) & 1u;
+    const uint32_t m2 = (y << 2) >> (31u - m1);
+    const uint32_t l2 = (y << (3u + m1)) >> 31;
+    const bool lok = !l0 || !l1 || !l2;
+    level = !l0 ? 1u : !l1 ? m1 : m2;
+    const uint32_t llen = !l0 ? 1u : !l1 ? 3u : 4u + m1;                          // <= 7
+    return dok && lok ? dlen + 1u + llen : 0u;                                      // <= 31
+}
+
+constexpr uint32_t kDecodeStageWords = 2048;   // per wavefront
+
+// One bucket per lane.  Its nibble words are stored exactly once each, in
+// chunks of CW words (CW = 4: 16-byte stores, for d a multiple of 32 and a
+// 16-byte aligned output; else CW = 1) built in registers: a chunk is stored
+// when a coordinate lands past it, chunks with no coordinate as zeros.  The
+// loop runs while any lane of the wavefront is still reading, with the
+// common steps written as selects: the refill always loads a word (the
+// bucket's last one once past it) and keeps it only when needed, and a lane
+// that has stopped changes nothing.  Codes that do not fit the window's top
+// 32 bits, and the bucket's end, go through the general reader.
+template <uint32_t CW>
+struct NibChunk {
+    uint32_t c[CW];
+    __device__ void clear()
+    {
+#pragma unroll
+        for (uint32_t k = 0; k < CW; ++k)
+            c[k] = 0u;
+    }
+    __device__ void put(uint32_t q, uint32_t v)   // word q of the chunk |= v
+    {
+#pragma unroll
+        for (uint32_t k = 0; k < CW; ++k)
+            c[k] |= q == k ? v : 0u;
+    }
+    // chunk ch of the bucket's nw words
+    __device__ void store(uint32_t *__restrict__ nib, uint32_t ch, uint32_t nw) const
+    {
+        if constexpr (CW == 4) {
+            if (ch * 4u + 4u <= nw) {
+                uint4 v;
+                v.x = c[0];
+                v.y = c[1];
+                v.z = c[2];
+                v.w = c[3];
+                reinterpret_cast<uint4 *>(nib)[ch] = v;
+                return;
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < CW; ++k)
+            if (ch * CW + k < nw)
+                nib[ch * CW + k] = c[k];
+    }
+};
+
+template <uint32_t CW, typename Src>
+__device__ __forceinline__ void decode_bucket(Src src, uint64_t start, uint64_t end, uint32_t blen,
+                                              bool valid, float *norm_out,
+                                              uint32_t *__restrict__ nib)
+{
+    const uint64_t span = valid ? end - start : 0u;
+    BitReader<Src> r{src, 0u, span < (1ull << 31) ? (uint32_t)span : (1u << 31), 0u, 0u, valid};
+    const uint32_t lastw = span ? (uint32_t)(((end - 1u) >> 5) - (start >> 5)) : 0u;
+    const uint32_t nw = (blen + 7u) / 8u;                 // 0 for a lane with no bucket
+    const uint32_t nch = (nw + CW - 1u) / CW;
+    // the first word may begin mid-word: load it and drop the bits before
+    // the bucket
+    if (span) {
+        const uint32_t skip = (uint32_t)(start & 31u);
+        r.buf = ((uint64_t)src[r.word++] << 32) << skip;
+        r.avail = 32u - skip;
+    }
+    const float norm = __uint_as_float(r.get(32));
+    if (valid)
+        *norm_out = norm;
+    bool active = r.ok && r.left;
+    int32_t prev = -1;
+    NibChunk<CW> chunk;
+    chunk.clear();
+    uint32_t cur = 0;   // index of the chunk being built
+    while (__any(active)) {
+        const bool need = active && r.avail <= 32u && r.avail < r.left;
+        const uint32_t wv = span ? src[r.word < lastw ? r.word : lastw] : 0u;
+        r.buf |= need ? (uint64_t)wv << (32u - r.avail) : 0u;
+        r.word += need ? 1u : 0u;
+        r.avail += need ? 32u : 0u;
+        const uint32_t lim = r.avail < r.left ? r.avail : r.left;
+        uint32_t dist, sign, level;
+        const uint32_t len = coord_peek((uint32_t)(r.buf >> 32), dist, sign, level);
+        const bool fast = len && len <= lim;
+        const uint32_t take = active && fast ? len : 0u;
+        r.buf <<= take;
+        r.avail -= take;
+        r.left -= take;
+        if (active && !fast) {
+            dist = r.omega();
+            sign = r.get(1);
+            level = r.omega();
+        }
+        // li < blen <= 2048 unless the bucket stops here (dist < 2^31)
+        const uint32_t li = (uint32_t)(prev + 1) + (dist - 1u);
+        const bool ins = active && r.ok && li < blen && level <= 7u;
+        const uint32_t ch = li / (8u * CW);
+        if (ins && ch != cur) {   // later chunks only: the chunk before is done
+            chunk.store(nib, cur, nw);
+            chunk.clear();
+            while (++cur < ch)
+                chunk.store(nib, cur, nw);
+        }
+        chunk.put(ins ? (li >> 3) % CW : CW, ((sign << 3) | level) << (28u - 4u * (li & 7u)));
+        prev = ins ? (int32_t)li : prev;
+        active = ins && r.left;
+    }
+    // the last chunk, then zeros to the bucket's end
+    if (nch) {
+        chunk.store(nib, cur, nw);
+        chunk.clear();
+        while (++cur < nch)
+            chunk.store(nib, cur, nw);
+    }
+}
+
+// Vec: 16-byte nibble stores (d a multiple of 32, output 16-byte aligned).
+template <bool Vec>
 __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
     const uint32_t *__restrict__ in, const uint64_t *__restrict__ offs, uint64_t n, uint32_t d,
     uint64_t nb, uint64_t in_words, float *__restrict__ norms, uint32_t *__restrict__ nibbles)
 {
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-        const uint64_t lo = b * d;
-        const uint32_t blen = (uint32_t)(lo + d < n ? d : n - lo);
-        const uint32_t nw = (blen + 7u) / 8u;
-        uint32_t *nib = nibbles + (lo >> 3);
-        uint64_t start = offs[b], end = offs[b + 1];
-        if (end > in_words * 32u)
-            end = in_words * 32u;
-        if (start > end)
-            start = end;
-        BitReader r{in, start >> 5, end - start, 0u, 0u, true};
-        // the first word may begin mid-word: load it and drop the bits before
-        // the bucket
-        const uint32_t skip = (uint32_t)(start & 31u);
-        if (end > start) {
-            r.buf = (uint64_t)in[r.word++] << 32;
-            r.avail = 32u;
-            r.buf <<= skip;
-            r.avail -= skip;
+    __shared__ uint32_t stage[kBlockWaves][kDecodeStageWords];
+    const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const uint64_t nlanes_groups = (nb + kWave - 1) / kWave;                  // 64 buckets each
+    const uint64_t ngroups = (nlanes_groups + kBlockWaves - 1) / kBlockWaves;  // per workgroup
+    const uint64_t limit = in_words * 32u;
+    for (uint64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+        const uint64_t b = (grp * kBlockWaves + wave) * kWave + lane;
+        const bool valid = b < nb;
+        uint64_t start = 0, end = 0;
+        if (valid) {
+            start = offs[b];
+            end = offs[b + 1];
+            end = end < limit ? end : limit;
+            start = start < end ? start : end;
         }
-        norms[b] = __uint_as_float(r.get(32));
-        int64_t prev = -1;
-        uint32_t cur = 0, cur_w = 0;   // nibble word being built, and its index
-        while (r.ok && r.left) {
-            const int64_t li = prev + (int64_t)r.omega();
-            const uint32_t sign = r.get(1);
-            const uint32_t level = r.omega();
-            if (!r.ok || li >= (int64_t)blen || level > 7u)
-                break;
-            const uint32_t w = (uint32_t)li >> 3;
-            while (cur_w < w) {            // words before this coordinate are done
-                nib[cur_w++] = cur;
-                cur = 0;
-            }
-            cur |= ((sign << 3) | level) << (28u - 4u * ((uint32_t)li & 7u));
-            prev = li;
+        // the wavefront's word range: staged when it fits
+        uint64_t wlo = valid && end > start ? start >> 5 : ~0ull;
+        uint64_t whi = valid && end > start ? (end + 31u) >> 5 : 0u;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint64_t a = __shfl_xor(wlo, off, kWave), c = __shfl_xor(whi, off, kWave);
+            wlo = a < wlo ? a : wlo;
+            whi = c > whi ? c : whi;
         }
-        while (cur_w < nw) {
-            nib[cur_w++] = cur;
-            cur = 0;
+        const bool staged = whi <= wlo || whi - wlo <= kDecodeStageWords;
+        if (staged && whi > wlo) {
+            // every load issued before the first LDS store
+            const uint32_t cnt = (uint32_t)(whi - wlo);
+            uint32_t t[kDecodeStageWords / kWave];
+#pragma unroll
+            for (uint32_t j = 0; j < kDecodeStageWords / kWave; ++j)
+                if (lane + j * kWave < cnt)
+                    t[j] = in[wlo + lane + j * kWave];
+#pragma unroll
+            for (uint32_t j = 0; j < kDecodeStageWords / kWave; ++j)
+                if (lane + j * kWave < cnt)
+                    stage[wave][lane + j * kWave] = t[j];
         }
+        __syncthreads();
+        {
+            // every lane runs the loop (its trip count is the wavefront's);
+            // lanes past the last bucket read and store nothing
+            const uint64_t lo = valid ? b * d : 0u;
+            const uint32_t blen = valid ? (uint32_t)(lo + d < n ? d : n - lo) : 0u;
+            const uint32_t *src =
+                staged ? stage[wave] + (end > start ? (start >> 5) - wlo : 0u) : in + (start >> 5);
+            if (Vec)
+                decode_bucket<4, const uint32_t *>(src, start, end, blen, valid, norms + b,
+                                                   nibbles + (lo >> 3));
+            else
+                decode_bucket<1, const uint32_t *>(src, start, end, blen, valid, norms + b,
+                                                   nibbles + (lo >> 3));
+        }
+        __syncthreads();   // the stage is rewritten by the next group
     }
 }
 
@@ -305,9 +630,10 @@ hipError_t launch_elias_encode(const float *norms, const uint32_t *nibbles, uint
                                uint64_t *offs, uint32_t *out, uint64_t cap, hipStream_t stream)
 {
     const uint64_t nb = (n + d - 1) / d;
+    const uint64_t ngroups = (nb + kBlockWaves - 1) / kBlockWaves;
     if (nb) {
-        const uint32_t grid = grid_for(nb, 0);
-        elias_length_kernel<<<grid, kWave, 0, stream>>>(nibbles, n, d, nb, offs);
+        elias_length_kernel<<<grid_for(ngroups, kEliasBlocksPerCU), kBlockThreads, 0, stream>>>(
+            nibbles, n, d, nb, offs);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -320,11 +646,12 @@ hipError_t launch_elias_encode(const float *norms, const uint32_t *nibbles, uint
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    // LDS for one bucket: shift + norm + every coordinate at its longest code,
-    // plus the word a code may spill into
-    const uint32_t lds_words = (31u + 32u + d * max_coord_bits(d) + 31u) / 32u + 1u;
-    elias_write_kernel<<<grid_for(nb, 0), kWave, (size_t)lds_words * 4u, stream>>>(
-        norms, nibbles, n, d, nb, offs, out, cap, lds_words);
+    // bits of one bucket: shift + norm + every coordinate at its longest
+    // code, plus the word a code may spill into
+    const uint32_t region_words = (31u + 32u + d * max_coord_bits(d) + 31u) / 32u + 1u;
+    const size_t lds = ((size_t)d + 1u + (size_t)kBlockWaves * region_words) * 4u;
+    elias_write_kernel<<<grid_for(ngroups, kEliasBlocksPerCU), kBlockThreads, lds, stream>>>(
+        norms, nibbles, n, d, nb, offs, out, cap, region_words);
     return hipGetLastError();
 }
 
@@ -335,8 +662,13 @@ hipError_t launch_elias_decode(const uint32_t *in, const uint64_t *offs, uint64_
     const uint64_t nb = (n + d - 1) / d;
     if (!nb)
         return hipSuccess;
-    elias_decode_kernel<<<grid_for((nb + kBlockThreads - 1) / kBlockThreads, 0), kBlockThreads, 0,
-                          stream>>>(in, offs, n, d, nb, in_words, norms, nibbles);
+    const uint64_t ngroups = ((nb + kWave - 1) / kWave + kBlockWaves - 1) / kBlockWaves;
+    if (d % 32u == 0 && ((uintptr_t)nibbles & 15u) == 0)
+        elias_decode_kernel<true><<<grid_for(ngroups, 0), kBlockThreads, 0, stream>>>(
+            in, offs, n, d, nb, in_words, norms, nibbles);
+    else
+        elias_decode_kernel<false><<<grid_for(ngroups, 0), kBlockThreads, 0, stream>>>(
+            in, offs, n, d, nb, in_words, norms, nibbles);
     return hipGetLastError();
 }
 
