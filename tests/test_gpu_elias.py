@@ -158,3 +158,98 @@ def test_full_size_sampled(gpu):
         assert np.array_equal(got, _bits(wh, 0, int(oh[-1]))), b
         assert host(norms2[b:b + 1]).view(np.uint32)[0] == nm.view(np.uint32)[0]
         assert np.array_equal(host(nib2[b * d // 8:(b + 1) * d // 8]), clear_zero_level_signs(nb))
+
+
+def test_decode_into_unaligned_output(gpu):
+    # d a multiple of 32 with an output that is 4- but not 16-byte aligned:
+    # the word-by-word store path, against the oracle's decode
+    import torch
+
+    say("elias decode, unaligned output")
+    rs = np.random.default_rng(114)
+    for d in (256, 512):
+        n = 37 * d + 100
+        g = (rs.standard_normal(n) * 0.01).astype(np.float32)
+        norms, nib = oracle.qsgd_quantize(g, d, 7, 41 + d)
+        offs_h, words_h = oracle.qsgd_elias_encode(norms, nib, n, d)
+        nw = nib.size
+        buf = torch.full((nw + 8,), 0x3C3C3C3C, dtype=torch.int32, device="cuda")
+        out_n = torch.empty(norms.size, device="cuda")
+        gpu.qsgd_elias_decode(dev(words_h), dev(offs_h.astype(np.int64)), n, d, norms=out_n,
+                              nibbles=buf[1:1 + nw])
+        _, nb_h = oracle.qsgd_elias_decode(words_h, offs_h, n, d)
+        b = host(buf)
+        assert np.array_equal(b[1:1 + nw], nb_h), d
+        assert b[0] == 0x3C3C3C3C and np.all(b[1 + nw:] == 0x3C3C3C3C)
+        assert np.array_equal(host(out_n).view(np.uint32), norms.view(np.uint32))
+
+
+def _reference_truncated_decode(words, offs, n, d, in_count):
+    """The decode contract on an input cut to in_count words, bit by bit in
+    Python: no bit past the cut or past a bucket's end is read; a norm needs
+    its 32 bits (else 0); a coordinate whose codes do not all fit, or whose
+    index or level is out of range, stops the bucket; uncoded coordinates
+    get nibble 0.  Omega codes: groups of a 1 and k more digits, ended by 0."""
+    bits = np.unpackbits(np.ascontiguousarray(words[:in_count]).astype(">u4").view(np.uint8))
+    limit = in_count * 32
+    nb = (n + d - 1) // d
+    norms = np.zeros(nb, np.uint32)
+    nib = np.zeros((n + 7) // 8, np.uint32)
+    for b in range(nb):
+        blen = min(d, n - b * d)
+        start, end = int(offs[b]), min(int(offs[b + 1]), limit)
+        start = min(start, end)
+        st = {"pos": start, "ok": True}
+
+        def get(k):
+            if not st["ok"] or st["pos"] + k > end:
+                st["ok"] = False
+                return 0
+            v = 0
+            for i in range(k):
+                v = (v << 1) | int(bits[st["pos"] + i])
+            st["pos"] += k
+            return v
+
+        def omega():
+            k = 1
+            while st["ok"] and get(1):
+                if k >= 31:
+                    st["ok"] = False
+                    return 0
+                k = (1 << k) | get(k)
+            return k
+
+        norms[b] = get(32)
+        prev = -1
+        while st["ok"] and st["pos"] < end:
+            li = prev + omega()
+            sign = get(1)
+            level = omega()
+            if not st["ok"] or li >= blen or level > 7:
+                break
+            i = b * d + li
+            nib[i // 8] |= np.uint32(((sign << 3) | level) << (28 - 4 * (i % 8)))
+            prev = li
+    return norms, nib
+
+
+@pytest.mark.parametrize("d", [64, 512, 1000])
+def test_decode_of_a_truncated_input(gpu, d):
+    # the input cut short at several word counts: buckets before the cut decode
+    # as usual, the bucket across it keeps its whole coordinates, later ones
+    # come out as zeros; nothing past the cut is read
+    say("elias truncated input d", d)
+    rs = np.random.default_rng(115 + d)
+    n = 12 * d + 7
+    g = (rs.standard_normal(n) * 0.01).astype(np.float32)
+    g[rs.integers(0, n, n // 30)] *= np.float32(200.0)
+    norms, nib = oracle.qsgd_quantize(g, d, 7, 51 + d)
+    offs_h, words_h = oracle.qsgd_elias_encode(norms, nib, n, d)
+    offs_d = dev(offs_h.astype(np.int64))
+    total = words_h.size
+    for cut in sorted({1, 2, total // 5, total // 2 + 3, total - 1, total}):
+        want_n, want_nib = _reference_truncated_decode(words_h, offs_h, n, d, cut)
+        got_n, got_nib = gpu.qsgd_elias_decode(dev(words_h[:cut]), offs_d, n, d)
+        assert np.array_equal(host(got_n).view(np.uint32), want_n), (d, cut)
+        assert np.array_equal(host(got_nib), want_nib), (d, cut)
