@@ -166,13 +166,15 @@ def main():
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / K
-    op_ms = {op: sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(K)) / K
-             for j, op in enumerate(OPS)}
+    op_steps = {op: [ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(K)]
+                for j, op in enumerate(OPS)}
+    op_ms = {op: sum(v) / K for op, v in op_steps.items()}
     ops = {}
     for op in OPS:
         s = op_ms[op] / 1e3
         gbps = BYTES[op] * n / s / 1e9
-        ops[op] = {"ms": round(op_ms[op], 4), "elements_per_s": n / s,
+        ops[op] = {"ms": round(op_ms[op], 4), "ms_median": round(float(np.median(op_steps[op])), 4),
+                   "ms_best": round(min(op_steps[op]), 4), "elements_per_s": n / s,
                    "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                    "bytes_per_element": BYTES[op]}
 
