@@ -133,7 +133,8 @@ def test_average_workers(knobs, K):
     for dbpc, nt in ((0, 1), (3, 0)):
         gpu.set_tuning(qsgd_dequant_blocks_per_cu=dbpc, qsgd_dequant_nt=nt)
         for n, d in ((2048, 512), (2049, 512), (100_003, 512), (65_536 + 17, 256), (10_000, 1000),
-                     (50_000, 4096), (9_000, 64), (777, 1), (20_000, 255)):
+                     (50_000, 4096), (9_000, 64), (777, 1), (20_000, 255), (30_000, 341),
+                     (30_000, 340)):
             scales, nibs = _messages(gpu, K, n, d, 7, K * 31 + n % 97, maxnorm=(n % 2 == 1))
             check_average(gpu, scales, nibs, n, d, 7)
 
