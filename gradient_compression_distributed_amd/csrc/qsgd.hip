@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_lanes_kernel(
 // table read and an add; no division per element.  Sums are staged through
 // LDS so every store instruction writes 1 KiB.
 constexpr uint64_t kAvgTileElems = 8u * kBlockThreads;
-constexpr uint32_t kAvgChunk = 8;   // worker words loaded before they are decoded
+constexpr uint32_t kAvgChunk = 16;   // worker words loaded before they are decoded
 // table rows per worker: the buckets a 2048-element tile can touch when
 // d >= 228 (2047/d + 2 <= 10); smaller buckets take the per-element kernel
 constexpr uint32_t kAvgSlots = 10;
@@ -557,8 +557,8 @@ constexpr uint32_t kAvgWorkerBytes = kAvgSlots * 64u;
 // nibbles, times 4 (a byte offset into a 16-float table row), are spread
 // one per byte -- elements 0, 2, 4, 6 in `hi`, 1, 3, 5, 7 in `lo`, first
 // element in the top byte -- so each element's table address is its row
-// (off, which already holds the chunk's worker base) plus one byte of a
-// register, and the worker's place in the chunk is the LDS instruction's
+// (off, which already holds the group's worker base) plus one byte of a
+// register, and the worker's place in the group is the LDS instruction's
 // immediate offset.  The empty asm keeps the compiler from folding the
 // byte extraction back into a shift-and-mask per element.  All eight table
 // reads are issued before the additions.
@@ -579,6 +579,36 @@ __device__ __forceinline__ void avg_word(float (&a)[8], uint32_t w, const char *
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         a[e] += t[e];
+}
+
+// Workers l .. l+N-1 (their words w[0..N-1] already loaded), in order.
+template <uint32_t N, uint32_t J = 0>
+__device__ __forceinline__ void avg_words(float (&a)[8], const uint32_t (&w)[kAvgChunk],
+                                          const char *tb, const uint32_t (&offc)[8])
+{
+    if constexpr (J < N) {
+        avg_word<J>(a, w[J], tb, offc);
+        avg_words<N, J + 1>(a, w, tb, offc);
+    }
+}
+
+template <uint32_t N, bool NT>
+__device__ __forceinline__ void avg_group(float (&a)[8], uint32_t (&w)[kAvgChunk], bool loaded,
+                                          const QsgdMsgs &ms, uint32_t l, uint64_t wi,
+                                          const char *tb, const uint32_t (&off)[8])
+{
+    if (!loaded) {
+#pragma unroll
+        for (uint32_t j = 0; j < N; ++j)
+            w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l + j] + wi);
+    }
+    uint32_t offc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        offc[e] = off[e] + l * kAvgWorkerBytes;
+        asm volatile("" : "+v"(offc[e]));   // one add per group, not per read
+    }
+    avg_words<N>(a, w, tb, offc);
 }
 
 template <bool Pow2K, bool NT>
@@ -602,13 +632,19 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
         __syncthreads();   // the previous tile is done with the table and the stage
         const uint64_t wi = (e_tile >> 3) + tid;
         const bool valid = wi < nwords;
-        // the first chunk's nibble words do not depend on the table: their
-        // loads are issued before it is built
+        // the first group's nibble words do not depend on the table: their
+        // loads are issued before it is built (16 workers, or 8 for K < 16)
         uint32_t w[kAvgChunk];
-        if (valid && K >= kAvgChunk) {
+        const uint32_t first = K >= 16u ? 16u : (K >= 8u ? 8u : 0u);
+        if (valid && first) {
 #pragma unroll
-            for (uint32_t j = 0; j < kAvgChunk; ++j)
+            for (uint32_t j = 0; j < 8; ++j)
                 w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
+            if (first == 16u) {
+#pragma unroll
+                for (uint32_t j = 8; j < 16; ++j)
+                    w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
+            }
         }
         // thread (l, nib) = (tid / 16 + 16 j, tid % 16) fills nibble nib of
         // worker l for every bucket of the tile; its scale loads are issued
@@ -651,29 +687,12 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
             for (int e = 0; e < 8; ++e)
                 off[e] = (bb0 + ((uint32_t)e >= brk ? 1u : 0u)) * 64u;
             const char *tb = (const char *)table;
+            // groups of 16, then 8 workers: every load issued, then decoded
             uint32_t l = 0;
-            // groups of kAvgChunk workers: every load issued, then decoded
-            for (; l + kAvgChunk <= K; l += kAvgChunk) {
-                if (l) {
-#pragma unroll
-                    for (uint32_t j = 0; j < kAvgChunk; ++j)
-                        w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l + j] + wi);
-                }
-                uint32_t offc[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    offc[e] = off[e] + l * kAvgWorkerBytes;
-                    asm volatile("" : "+v"(offc[e]));   // one add per chunk, not per read
-                }
-                avg_word<0>(a, w[0], tb, offc);
-                avg_word<1>(a, w[1], tb, offc);
-                avg_word<2>(a, w[2], tb, offc);
-                avg_word<3>(a, w[3], tb, offc);
-                avg_word<4>(a, w[4], tb, offc);
-                avg_word<5>(a, w[5], tb, offc);
-                avg_word<6>(a, w[6], tb, offc);
-                avg_word<7>(a, w[7], tb, offc);
-            }
+            for (; l + 16u <= K; l += 16u)
+                avg_group<16, NT>(a, w, l == 0, ms, l, wi, tb, off);
+            for (; l + 8u <= K; l += 8u)
+                avg_group<8, NT>(a, w, l == 0, ms, l, wi, tb, off);
             for (; l < K; ++l) {
                 uint32_t offc[8];
 #pragma unroll
