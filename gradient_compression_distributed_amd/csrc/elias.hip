@@ -600,14 +600,16 @@ __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
             // lanes past the last bucket read and store nothing
             const uint64_t lo = valid ? b * d : 0u;
             const uint32_t blen = valid ? (uint32_t)(lo + d < n ? d : n - lo) : 0u;
-            const uint32_t *src =
-                staged ? stage[wave] + (end > start ? (start >> 5) - wlo : 0u) : in + (start >> 5);
-            if (Vec)
-                decode_bucket<4, const uint32_t *>(src, start, end, blen, valid, norms + b,
-                                                   nibbles + (lo >> 3));
+            // separate calls, so that each reads through its own address space
+            // (LDS reads for the staged copy, not generic loads)
+            constexpr uint32_t CW = Vec ? 4u : 1u;
+            if (staged)
+                decode_bucket<CW, const uint32_t *>(
+                    stage[wave] + (end > start ? (start >> 5) - wlo : 0u), start, end, blen, valid,
+                    norms + b, nibbles + (lo >> 3));
             else
-                decode_bucket<1, const uint32_t *>(src, start, end, blen, valid, norms + b,
-                                                   nibbles + (lo >> 3));
+                decode_bucket<CW, const uint32_t *>(in + (start >> 5), start, end, blen, valid,
+                                                    norms + b, nibbles + (lo >> 3));
         }
         __syncthreads();   // the stage is rewritten by the next group
     }
