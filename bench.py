@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "gc2_quantize elements/s and achieved HBM GB/s (% of peak) at 1G fp32 elems"
 HBM_PEAK_GBPS = 8000.0
 W_WORKERS = 16
+SAPS_C = 100.0   # the SAPS page's example keeps 1% of the components
 QSGD_D, QSGD_S = 512, 7
 # algorithmic HBM bytes per element of each operation
 BYTES = {
@@ -251,7 +252,7 @@ def main():
         # SAPS shared-seed sparsification at c = 100 (99% of the components
         # dropped): mask (+ offsets), gather of the kept components, merge of a
         # peer's; algorithmic bytes count the mask bits and the kept elements
-        c_saps, seed_saps = 100.0, wl.qsgd_seed(9)
+        c_saps, seed_saps = SAPS_C, wl.qsgd_seed(9)
         smask = torch.empty(gcq.saps_mask_words(n), dtype=torch.int32, device=dev)
         soffs = torch.empty(gcq.saps_num_tiles(n) + 1, dtype=torch.int64, device=dev)
         mask_ms = timed(lambda: gcq.saps_mask(n, c_saps, seed_saps, mask=smask, offsets=soffs))
@@ -369,6 +370,40 @@ def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
         total += t4 - t0
         elems += blk
         b += 1
+    # the widened rows, timed the same way on a 2^21-element sample of the
+    # same gradient (inputs that are another row's output are made untimed)
+    m = 1 << 21
+    gs = g_dev[:m].cpu().numpy()
+    cfg7 = wl.CONFIGS[7]
+    rs = np.random.default_rng(7)
+    nxt = {}
+
+    def rate(fn):
+        t0 = time.perf_counter()
+        fn()
+        return m / (time.perf_counter() - t0)
+
+    rr, ww = np.zeros(m, np.float32), (rs.standard_normal(m) * cfg7.w_sigma).astype(np.float32)
+    nxt["cdsgd_update_quantize"] = rate(lambda: oracle.cdsgd_update_quantize(gs, rr, ww, cfg7.t,
+                                                                             cfg7.eta))
+    nxt["cdsgd_local_update"] = rate(lambda: oracle.cdsgd_local_update(gs, ww, cfg7.eta))
+    nxt["qsgd_quantize_maxnorm"] = rate(lambda: oracle.qsgd_quantize_maxnorm(gs, QSGD_D, QSGD_S,
+                                                                             wl.qsgd_seed(7)))
+    msgs = [oracle.qsgd_quantize(gs, QSGD_D, QSGD_S, wl.qsgd_seed(200 + k)) for k in range(W_WORKERS)]
+    nxt["qsgd_dequant_average"] = rate(lambda: oracle.qsgd_dequant_average(
+        [x[0] for x in msgs], [x[1] for x in msgs], m, QSGD_D, QSGD_S))
+    coded = {}
+    nxt["qsgd_elias_encode"] = rate(lambda: coded.setdefault(
+        "c", oracle.qsgd_elias_encode(msgs[0][0], msgs[0][1], m, QSGD_D)))
+    nxt["qsgd_elias_decode"] = rate(lambda: oracle.qsgd_elias_decode(coded["c"][1], coded["c"][0],
+                                                                      m, QSGD_D))
+    xs = (rs.standard_normal(m)).astype(np.float32)
+    kept = {}
+    nxt["saps_mask_and_gather"] = rate(lambda: kept.setdefault(
+        "v", oracle.saps_gather(xs, SAPS_C, wl.qsgd_seed(5))))
+    peer = rs.standard_normal(kept["v"].size).astype(np.float32)
+    nxt["saps_merge"] = rate(lambda: oracle.saps_merge(xs, SAPS_C, wl.qsgd_seed(5), peer))
+
     model = ""
     try:
         for ln in open("/proc/cpuinfo"):
@@ -382,6 +417,10 @@ def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
                       "all four operations, single thread pinned to one core",
             "seconds": round(total, 3),
             "ops_elements_per_s": {op: elems / s for op, s in per_op.items()},
+            "next_ops_elements_per_s": nxt,
+            "next_ops_sample": f"{m} elements of the same gradient, each widened operation once "
+                               f"(K = {W_WORKERS} messages for the average, c = {SAPS_C} for SAPS); "
+                               "arrays of this size stay in the host's caches",
             "host_cpus": os.cpu_count(), "cpu_model": model}
 
 
