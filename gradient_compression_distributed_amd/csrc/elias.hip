@@ -401,18 +401,17 @@ struct BitReader {
     }
 };
 
-// One coordinate from the top 32 bits x of the window (next bit in bit 31):
-// omega(dist) with at most 3 groups, the sign, omega(level) with at most 2
-// groups, all read with shifts and selects (no branches).  An omega code is
-// groups, each a 1 and k more digits making the next k, ended by a 0; the
-// first group starts from k = 1.  Returns the code's length, or 0 when it
-// needs more groups (more than 31 bits); the caller checks it against the
-// bits the window holds.
-__device__ __forceinline__ uint32_t coord_peek(uint32_t x, uint32_t &dist, uint32_t &sign,
-                                               uint32_t &level)
+// Omega codes read from the top 32 bits x of the window (next bit in bit
+// 31) with shifts and selects, no branches.  An omega code is groups, each a
+// 1 and k more digits making the next k, ended by a 0; the first group
+// starts from k = 1.
+//
+// omega(dist) with at most 3 groups: its length (<= 23), or 0 when it needs
+// more groups.
+__device__ __forceinline__ uint32_t dist_peek(uint32_t x, uint32_t &dist)
 {
-    // omega(dist): continuation bits c0..c3, group values k1 (2 bits), k2
-    // (k1 + 1 bits), k3 (k2 + 1 bits)
+    // continuation bits c0..c3, group values k1 (2 bits), k2 (k1 + 1 bits),
+    // k3 (k2 + 1 bits)
     const uint32_t c0 = x >> 31;
     const uint32_t k1 = 2u | ((x >> 30) & 1u);
     const uint32_t c1 = (x >> 29) & 1u;
@@ -420,33 +419,64 @@ __device__ __forceinline__ uint32_t coord_peek(uint32_t x, uint32_t &dist, uint3
     const uint32_t c2 = (x << (3u + k1)) >> 31;
     const uint32_t k3 = (x << (3u + k1)) >> (31u - k2);          // k2 <= 15
     const uint32_t c3 = (x << (4u + k1 + k2)) >> 31;
-    const bool dok = !c0 || !c1 || !c2 || !c3;
     dist = !c0 ? 1u : !c1 ? k1 : !c2 ? k2 : k3;
-    const uint32_t dlen = !c0 ? 1u : !c1 ? 3u : !c2 ? 4u + k1 : 5u + k1 + k2;   // <= 23
-    sign = (x << dlen) >> 31;
-    const uint32_t y = x << (dlen + 1u);
+    const uint32_t dlen = !c0 ? 1u : !c1 ? 3u : !c2 ? 4u + k1 : 5u + k1 + k2;
+    return !c0 || !c1 || !c2 || !c3 ? dlen : 0u;
+}
+
+// The sign bit, then omega(level) with at most 2 groups: their length
+// (<= 8), or 0 when the level code needs more groups.
+__device__ __forceinline__ uint32_t sign_level_peek(uint32_t x, uint32_t &sign, uint32_t &level)
+{
+    sign = x >> 31;
+    const uint32_t y = x << 1;
     const uint32_t l0 = y >> 31;
     const uint32_t m1 = 2u | ((y >> 30) & 1u);
     const uint32_t l1 = (y >> 29) & 1u;
     const uint32_t m2 = (y << 2) >> (31u - m1);
     const uint32_t l2 = (y << (3u + m1)) >> 31;
-    const bool lok = !l0 || !l1 || !l2;
     level = !l0 ? 1u : !l1 ? m1 : m2;
-    const uint32_t llen = !l0 ? 1u : !l1 ? 3u : 4u + m1;                          // <= 7
-    return dok && lok ? dlen + 1u + llen : 0u;                                      // <= 31
+    const uint32_t llen = !l0 ? 1u : !l1 ? 3u : 4u + m1;
+    return !l0 || !l1 || !l2 ? 1u + llen : 0u;
+}
+
+// One coordinate: omega(dist), the sign, omega(level).  Returns the code's
+// length (<= 31), or 0 when it needs more groups; the caller checks it
+// against the bits the window holds.
+__device__ __forceinline__ uint32_t coord_peek(uint32_t x, uint32_t &dist, uint32_t &sign,
+                                               uint32_t &level)
+{
+    const uint32_t dlen = dist_peek(x, dist);
+    const uint32_t slen = sign_level_peek(x << (dlen ? dlen : 1u), sign, level);
+    return dlen && slen ? dlen + slen : 0u;
 }
 
 constexpr uint32_t kDecodeStageWords = 2048;   // per wavefront
 
-// One bucket per lane.  Its nibble words are stored exactly once each, in
-// chunks of CW words (CW = 4: 16-byte stores, for d a multiple of 32 and a
-// 16-byte aligned output; else CW = 1) built in registers: a chunk is stored
-// when a coordinate lands past it, chunks with no coordinate as zeros.  The
-// loop runs while any lane of the wavefront is still reading, with the
-// common steps written as selects: the refill always loads a word (the
-// bucket's last one once past it) and keeps it only when needed, and a lane
-// that has stopped changes nothing.  Codes that do not fit the window's top
-// 32 bits, and the bucket's end, go through the general reader.
+// Decode tables for the common short codes (built per workgroup):
+//   distance table, indexed by the window's next 11 bits: (length << 8) |
+//   distance when omega(distance) fits those 11 bits (distances up to 31),
+//   else 0;
+//   sign-and-level table, indexed by the next 7 bits after the distance:
+//   ((1 + length) << 4) | nibble when the sign bit and omega(level) fit them
+//   with a level up to 7, else 0.
+// A coordinate whose codes miss either table goes through coord_peek.
+constexpr uint32_t kDistBits = 11, kLevelBits = 7;
+
+__device__ __forceinline__ uint32_t dist_entry(uint32_t i)
+{
+    uint32_t dist;
+    const uint32_t dlen = dist_peek(i << (32u - kDistBits), dist);
+    return dlen && dlen <= kDistBits ? (dlen << 8) | dist : 0u;
+}
+
+__device__ __forceinline__ uint32_t level_entry(uint32_t j)
+{
+    uint32_t sign, level;
+    const uint32_t slen = sign_level_peek(j << (32u - kLevelBits), sign, level);
+    return slen && slen <= kLevelBits && level <= 7u ? (slen << 4) | (sign << 3) | level : 0u;
+}
+
 template <uint32_t CW>
 struct NibChunk {
     uint32_t c[CW];
@@ -486,7 +516,8 @@ struct NibChunk {
 template <uint32_t CW, typename Src>
 __device__ __forceinline__ void decode_bucket(Src src, uint64_t start, uint64_t end, uint32_t blen,
                                               bool valid, float *norm_out,
-                                              uint32_t *__restrict__ nib)
+                                              uint32_t *__restrict__ nib,
+                                              const uint16_t *dist_tab, const uint8_t *level_tab)
 {
     const uint64_t span = valid ? end - start : 0u;
     BitReader<Src> r{src, 0u, span < (1ull << 31) ? (uint32_t)span : (1u << 31), 0u, 0u, valid};
@@ -515,8 +546,13 @@ __device__ __forceinline__ void decode_bucket(Src src, uint64_t start, uint64_t 
         r.word += need ? 1u : 0u;
         r.avail += need ? 32u : 0u;
         const uint32_t lim = r.avail < r.left ? r.avail : r.left;
-        uint32_t dist, sign, level;
-        const uint32_t len = coord_peek((uint32_t)(r.buf >> 32), dist, sign, level);
+        const uint32_t x = (uint32_t)(r.buf >> 32);
+        const uint32_t e1 = dist_tab[x >> (32u - kDistBits)];
+        const uint32_t e2 = level_tab[(x << (e1 >> 8)) >> (32u - kLevelBits)];
+        uint32_t dist = e1 & 0xFFu, sign = (e2 >> 3) & 1u, level = e2 & 7u;
+        uint32_t len = e1 && e2 ? (e1 >> 8) + (e2 >> 4) : 0u;
+        if (active && !len)   // a code the tables do not hold
+            len = coord_peek(x, dist, sign, level);
         const bool fast = len && len <= lim;
         const uint32_t take = active && fast ? len : 0u;
         r.buf <<= take;
@@ -557,7 +593,14 @@ __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
     uint64_t nb, uint64_t in_words, float *__restrict__ norms, uint32_t *__restrict__ nibbles)
 {
     __shared__ uint32_t stage[kBlockWaves][kDecodeStageWords];
+    __shared__ uint16_t dist_tab[1u << kDistBits];
+    __shared__ uint8_t level_tab[1u << kLevelBits];
     const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (uint32_t i = threadIdx.x; i < (1u << kDistBits); i += kBlockThreads)
+        dist_tab[i] = (uint16_t)dist_entry(i);
+    for (uint32_t j = threadIdx.x; j < (1u << kLevelBits); j += kBlockThreads)
+        level_tab[j] = (uint8_t)level_entry(j);
+    // (the first __syncthreads below orders the tables before any use)
     const uint64_t nlanes_groups = (nb + kWave - 1) / kWave;                  // 64 buckets each
     const uint64_t ngroups = (nlanes_groups + kBlockWaves - 1) / kBlockWaves;  // per workgroup
     const uint64_t limit = in_words * 32u;
@@ -606,10 +649,11 @@ __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
             if (staged)
                 decode_bucket<CW, const uint32_t *>(
                     stage[wave] + (end > start ? (start >> 5) - wlo : 0u), start, end, blen, valid,
-                    norms + b, nibbles + (lo >> 3));
+                    norms + b, nibbles + (lo >> 3), dist_tab, level_tab);
             else
                 decode_bucket<CW, const uint32_t *>(in + (start >> 5), start, end, blen, valid,
-                                                    norms + b, nibbles + (lo >> 3));
+                                                    norms + b, nibbles + (lo >> 3), dist_tab,
+                                                    level_tab);
         }
         __syncthreads();   // the stage is rewritten by the next group
     }
