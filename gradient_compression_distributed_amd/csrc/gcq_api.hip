@@ -81,11 +81,14 @@ int launch_status(hipError_t e)
     return GCQ_ERR_LAUNCH;
 }
 
-// Device tables of the fused launch: per device a ring of slots, each a
-// pinned host staging buffer, a device buffer and an event recorded after
-// the kernel that reads it.  A slot is reused only once its event has
-// completed, so a call never overwrites a table still in use; the copy and
-// the kernel are ordered on the caller's stream.
+// Device tables of the fused launch: per device a cache of slots, each a
+// pinned host copy of the table, a device buffer and an event recorded
+// after the last kernel that read it.  A call whose descriptors match a
+// slot's reuses that slot's device table; a new table goes to the least
+// recently used slot, rewritten only once its event has completed, so a
+// call never overwrites a table still in use.  The copy and the kernel are
+// ordered on the caller's stream.  All slots are allocated together on the
+// first call (and again only when a call has more buckets than they hold).
 constexpr int kRing = 8;
 constexpr int kMaxDevices = 64;
 
@@ -93,6 +96,8 @@ struct Slot {
     Gc2Desc *host = nullptr;
     Gc2Desc *dev = nullptr;
     size_t cap = 0;
+    size_t count = 0;       // descriptors of the table it holds (0: none)
+    uint64_t used = 0;      // call number of its last use
     hipEvent_t ev = nullptr;
     bool pending = false;
 };
@@ -100,13 +105,13 @@ struct Slot {
 struct DeviceRing {
     std::mutex mu;
     Slot slots[kRing];
-    unsigned next = 0;
-    int last = -1;          // slot holding the most recently uploaded table
-    size_t last_count = 0;  // its number of descriptors
+    uint64_t calls = 0;
 };
 
 DeviceRing g_rings[kMaxDevices];
 
+// A slot able to hold nb descriptors.  Growing frees the old buffers, so
+// the slot's last kernel must have completed (the caller waits for it).
 int ensure_capacity(Slot &s, size_t nb)
 {
     if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
@@ -121,6 +126,7 @@ int ensure_capacity(Slot &s, size_t nb)
     s.host = nullptr;
     s.dev = nullptr;
     s.cap = 0;
+    s.count = 0;
     if (hipHostMalloc((void **)&s.host, cap * sizeof(Gc2Desc), hipHostMallocDefault) != hipSuccess)
         return GCQ_ERR_NOMEM;
     if (hipMalloc((void **)&s.dev, cap * sizeof(Gc2Desc)) != hipSuccess) {
@@ -234,38 +240,62 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
     hipStream_t hs = (hipStream_t)stream;
     DeviceRing &ring = g_rings[dev];
     std::lock_guard<std::mutex> lock(ring.mu);
-    // The same buckets as the previous call (the usual case: fusion buckets
-    // are fixed across training steps): the table already on the device is
-    // reused as is.  The stream first waits for the slot's event (recorded
-    // after the last kernel that read the table, itself after the upload),
-    // so the upload is complete whatever stream made it, and the event then
-    // re-recorded covers every kernel that used the slot: a slot is only
-    // rewritten once all of them have finished.
+    ++ring.calls;
+    // The same buckets as an earlier call (the usual case: fusion buckets are
+    // fixed across training steps, possibly a few alternating sets): the
+    // table already on the device is reused as is.  The stream first waits
+    // for the slot's event (recorded after the last kernel that read the
+    // table, itself after the upload), so the upload is complete whatever
+    // stream made it, and the event then re-recorded covers every kernel that
+    // used the slot: a slot is only rewritten once all of them have finished.
     Slot *sp = nullptr;
-    if (ring.last >= 0 && ring.last_count == num_buckets &&
-        memcmp(ring.slots[ring.last].host, descs.data(), bytes) == 0) {
-        sp = &ring.slots[ring.last];
+    for (Slot &c : ring.slots) {
+        if (c.count == num_buckets && memcmp(c.host, descs.data(), bytes) == 0) {
+            sp = &c;
+            break;
+        }
+    }
+    if (sp) {
         if (sp->pending && hipStreamWaitEvent(hs, sp->ev, 0) != hipSuccess)
             return GCQ_ERR_LAUNCH;
     } else {
-        const int idx = (int)(ring.next++ % kRing);
-        Slot &s = ring.slots[idx];
+        Slot *lru = &ring.slots[0];
+        for (Slot &c : ring.slots)
+            if (c.used < lru->used)
+                lru = &c;
+        Slot &s = *lru;
         if (s.pending) {
             if (hipEventSynchronize(s.ev) != hipSuccess)
                 return GCQ_ERR_LAUNCH;
             s.pending = false;
         }
-        ring.last = -1;
+        s.count = 0;
+        if (s.cap < num_buckets) {
+            // every free slot grows with it, so later new tables of this size
+            // allocate nothing
+            for (Slot &c : ring.slots) {
+                if (c.cap >= num_buckets)
+                    continue;
+                if (c.pending) {
+                    if (hipEventSynchronize(c.ev) != hipSuccess)
+                        return GCQ_ERR_LAUNCH;
+                    c.pending = false;
+                }
+                int st = ensure_capacity(c, num_buckets);
+                if (st != GCQ_OK)
+                    return st;
+            }
+        }
         int st = ensure_capacity(s, num_buckets);
         if (st != GCQ_OK)
             return st;
         memcpy(s.host, descs.data(), bytes);
         if (hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess)
             return GCQ_ERR_LAUNCH;
-        ring.last = idx;
-        ring.last_count = num_buckets;
+        s.count = num_buckets;
         sp = &s;
     }
+    sp->used = ring.calls;
     Slot &s = *sp;
     hipError_t e = gcq::launch_gc2_table(tu, s.dev, num_buckets, total_tiles, (uint32_t)tpb, hs);
     if (e != hipSuccess)

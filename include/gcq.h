@@ -111,7 +111,10 @@ typedef struct gc2_bucket {
  *
  *   buckets      host array of num_buckets descriptors; read during the
  *                call only (the library copies it into a library-owned,
- *                stream-ordered device table, grown on demand)
+ *                stream-ordered device table, or reuses one of the last 8
+ *                distinct tables it uploaded when the descriptors match;
+ *                the tables are allocated on the first call and grown on
+ *                demand)
  *   num_buckets  0 .. 2^31-1
  *   stream       hipStream_t
  *

@@ -305,6 +305,50 @@ def test_bucket_table_reuse_across_streams(gpu):
             assert np.array_equal(bits(host(r_d[i])), bits(r_h[i])), (step, i)
 
 
+def test_bucket_table_cache_over_many_lists(gpu):
+    # several bucket lists in rotation (each reused from the device table
+    # cache), then more distinct lists than the cache holds (least recently
+    # used tables evicted while their kernels may still run), and a longer
+    # list that makes the slots grow; every call matches the oracle
+    import torch
+
+    say("gc2 table cache over many lists")
+    rs = np.random.default_rng(32)
+    t = 0.03
+    lists, host_state = [], []
+    for k in range(12):
+        sizes = [int(x) for x in rs.integers(100, 9000, 1 + k % 3)]
+        gs = [(rs.standard_normal(n) * 0.03).astype(np.float32) for n in sizes]
+        g_d = [dev(a) for a in gs]
+        r_d = [torch.zeros(n, device="cuda") for n in sizes]
+        o_d = [torch.empty(oracle.packed_words(n), dtype=torch.int32, device="cuda") for n in sizes]
+        lists.append((gpu.BucketList([(g_d[i], r_d[i], o_d[i], t) for i in range(len(sizes))]),
+                      r_d, o_d))
+        host_state.append((gs, [np.zeros(n, np.float32) for n in sizes]))
+    # a rotation over 3 lists, then all 12 twice, then a 40-bucket list
+    order = [0, 1, 2] * 4 + list(range(12)) * 2
+    for j, k in enumerate(order):
+        bl, r_d, o_d = lists[k]
+        gpu.gc2_quantize_buckets(bl)
+        gs, r_h = host_state[k]
+        want = [oracle.gc2_quantize(gs[i], r_h[i], t) for i in range(len(gs))]
+        if j % 5 == 4:   # let several launches queue up between checks
+            torch.cuda.synchronize()
+            for i in range(len(gs)):
+                assert np.array_equal(host(o_d[i]), want[i]), (j, k, i)
+                assert np.array_equal(bits(host(r_d[i])), bits(r_h[i])), (j, k, i)
+    torch.cuda.synchronize()
+    big = [int(x) for x in rs.integers(50, 3000, 40)]
+    gs = [(rs.standard_normal(n) * 0.03).astype(np.float32) for n in big]
+    r_d = [torch.zeros(n, device="cuda") for n in big]
+    o_d = [torch.empty(oracle.packed_words(n), dtype=torch.int32, device="cuda") for n in big]
+    gpu.gc2_quantize_buckets(gpu.BucketList([(dev(gs[i]), r_d[i], o_d[i], t)
+                                              for i in range(len(big))]))
+    torch.cuda.synchronize()
+    for i in range(len(big)):
+        assert np.array_equal(host(o_d[i]), oracle.gc2_quantize(gs[i], np.zeros(big[i], np.float32), t))
+
+
 def _code_properties(w32, r_new, v, t):
     """Per-code facts that hold at any size (checked on the GPU with torch)."""
     import torch
