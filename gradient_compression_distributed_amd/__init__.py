@@ -45,7 +45,7 @@ class Tuning(ctypes.Structure):
         "gc2_unroll", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
         "dq_lds_stores", "dq_blocks_per_cu", "dq_fp4_decode", "qsgd_nt", "qsgd_rcp",
         "qsgd_dequant_nt", "qsgd_blocks_per_cu", "qsgd_dequant_blocks_per_cu",
-        "qsgd_buckets_per_wave")]
+        "qsgd_buckets_per_wave", "dq_words_per_thread")]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -46,6 +46,7 @@ __device__ __forceinline__ uint32_t signed_pairs(uint32_t w)
 //   t < 2^-120, where t/2 or t/64 would not be exact).
 enum { kDecodeFp4 = 0, kDecodeSdwa = 1, kDecodePlain = 2 };
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 // Byte B of the masked words: nibble 2B holds pair 14-4B (me) / 15-4B (mo),
 // nibble 2B+1 pair 12-4B / 13-4B.
@@ -184,6 +185,98 @@ __global__ __launch_bounds__(kBlockThreads) void dq_reduce_kernel(DqWorkers ws, 
     }
 }
 
+// Two packed words per thread (32 elements): one 8-byte load per worker
+// (the word arrays 8-byte aligned), a block tile of 512 words.  Sums of a
+// full tile leave through LDS as in dq_reduce_kernel: rows of 32 floats
+// padded to 36 (a 144-byte stride spreads the lanes' rows over the banks),
+// read back so that lane L stores elements 256q + 4L .. +3 (q = 0..7).
+constexpr int kRow2 = 36;   // floats per staged row
+
+template <int Mode, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlockThreads) void dq_reduce2_kernel(DqWorkers ws, uint32_t W,
+                                                                   uint32_t nwords, uint64_t n,
+                                                                   float tq, float *__restrict__ acc)
+{
+    __shared__ v4f stage[kBlockWaves * kWave * kRow2 / 4];
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    GCQ_GLOBAL float *out = (GCQ_GLOBAL float *)acc;
+    for (uint32_t base = blockIdx.x * 2u * kBlockThreads; base < nwords;
+         base += gridDim.x * 2u * kBlockThreads) {
+        const uint32_t wi = base + 2u * tid;   // the thread's first word
+        float a[16], b[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            a[k] = 0.0f;
+            b[k] = 0.0f;
+        }
+        if (wi + 1u < nwords) {
+            const uint32_t boff = wi * 4u;
+            uint32_t w0 = 0;
+            for (; w0 + kChunk <= W; w0 += kChunk) {
+                v2u wd[kChunk];
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j)
+                    wd[j] = ld<NTL>((const GCQ_GLOBAL v2u *)(
+                        (const GCQ_GLOBAL char *)ws.w[w0 + j] + boff));
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j) {
+                    accumulate<Mode>(a, wd[j].x, tq);
+                    accumulate<Mode>(b, wd[j].y, tq);
+                }
+            }
+            for (; w0 < W; ++w0) {
+                const v2u wd = ld<NTL>((const GCQ_GLOBAL v2u *)(
+                    (const GCQ_GLOBAL char *)ws.w[w0] + boff));
+                accumulate<Mode>(a, wd.x, tq);
+                accumulate<Mode>(b, wd.y, tq);
+            }
+        } else if (wi < nwords) {   // the last word alone
+            const uint32_t boff = wi * 4u;
+            for (uint32_t w0 = 0; w0 < W; ++w0)
+                accumulate<Mode>(a,
+                                 ld<NTL>((const GCQ_GLOBAL uint32_t *)(
+                                     (const GCQ_GLOBAL char *)ws.w[w0] + boff)),
+                                 tq);
+        }
+        const uint64_t e = (uint64_t)wi * 16u;
+        if (((uint64_t)base + 2u * kBlockThreads) * 16u <= n) {
+            v4f *rowp = stage + (wave * kWave + lane) * (kRow2 / 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v4f x, y;
+                x.x = a[4 * q];
+                x.y = a[4 * q + 1];
+                x.z = a[4 * q + 2];
+                x.w = a[4 * q + 3];
+                y.x = b[4 * q];
+                y.y = b[4 * q + 1];
+                y.z = b[4 * q + 2];
+                y.w = b[4 * q + 3];
+                rowp[q] = x;
+                rowp[4 + q] = y;
+            }
+            __syncthreads();
+            const uint64_t e0 = ((uint64_t)base + 2u * (uint64_t)wave * kWave) * 16u;
+            const v4f *wstage = stage + wave * kWave * (kRow2 / 4);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                // element 256q + 4L of the wave tile: row 8q + L/8, column 4(L%8)
+                const v4f x = wstage[(8 * q + (lane >> 3)) * (kRow2 / 4) + (lane & 7)];
+                st<NTS>((GCQ_GLOBAL v4f *)(out + e0) + 64 * q + lane, x);
+            }
+            __syncthreads();
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (e + k < n)
+                    out[e + k] = a[k];
+                if (e + 16 + k < n)
+                    out[e + 16 + k] = b[k];
+            }
+        }
+    }
+}
+
 template <int Mode, bool NTL, bool NTS, bool Lds>
 void launch_one(uint32_t grid, hipStream_t stream, const DqWorkers &ws, uint32_t W,
                 uint32_t nwords, uint64_t n, float tq, float *acc)
@@ -194,8 +287,22 @@ void launch_one(uint32_t grid, hipStream_t stream, const DqWorkers &ws, uint32_t
 
 template <int Mode>
 void dispatch(const gcq_tuning &tu, uint32_t grid, hipStream_t stream, const DqWorkers &ws,
-              uint32_t W, uint32_t nwords, uint64_t n, float tq, float *acc)
+              uint32_t W, uint32_t nwords, uint64_t n, float tq, float *acc, bool two)
 {
+    if (two) {
+        const uint32_t grid2 = grid_for((nwords + 2u * kBlockThreads - 1) / (2u * kBlockThreads),
+                                        tu.dq_blocks_per_cu);
+        const int k2 = tu.dq_nt_loads * 2 + tu.dq_nt_stores;
+        if (k2 == 3)
+            dq_reduce2_kernel<Mode, true, true><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+        else if (k2 == 2)
+            dq_reduce2_kernel<Mode, true, false><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+        else if (k2 == 1)
+            dq_reduce2_kernel<Mode, false, true><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+        else
+            dq_reduce2_kernel<Mode, false, false><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+        return;
+    }
     const int key = tu.dq_nt_loads * 4 + tu.dq_nt_stores * 2 + tu.dq_lds_stores;
     switch (key) {
     case 0: launch_one<Mode, false, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
@@ -233,12 +340,16 @@ hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, flo
             ws.w[k] = w.w[k] + w0;
         const uint32_t grid =
             grid_for((cw + kBlockThreads - 1) / kBlockThreads, tu.dq_blocks_per_cu);
+        // two words per thread when every word array is 8-byte aligned here
+        bool two = tu.dq_words_per_thread == 2;
+        for (uint32_t k = 0; k < W; ++k)
+            two = two && ((uintptr_t)ws.w[k] & 7u) == 0;
         if (mode == kDecodeFp4)
-            dispatch<kDecodeFp4>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
+            dispatch<kDecodeFp4>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16, two);
         else if (mode == kDecodeSdwa)
-            dispatch<kDecodeSdwa>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
+            dispatch<kDecodeSdwa>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16, two);
         else
-            dispatch<kDecodePlain>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16);
+            dispatch<kDecodePlain>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16, two);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -53,6 +53,7 @@ void init_locked()
     if (g_tuning.qsgd_buckets_per_wave != 1 && g_tuning.qsgd_buckets_per_wave != 2 &&
         g_tuning.qsgd_buckets_per_wave != 4)
         g_tuning.qsgd_buckets_per_wave = 0;
+    g_tuning.dq_words_per_thread = env_int("GCQ_DQ_WORDS_PER_THREAD", 2) == 1 ? 1 : 2;
     g_init = true;
 }
 
@@ -76,7 +77,8 @@ bool tuning_valid(const gcq_tuning &t)
            flag_ok(t.qsgd_rcp) && flag_ok(t.qsgd_dequant_nt) && count_ok(t.qsgd_blocks_per_cu) &&
            count_ok(t.qsgd_dequant_blocks_per_cu) &&
            (t.qsgd_buckets_per_wave == 0 || t.qsgd_buckets_per_wave == 1 ||
-            t.qsgd_buckets_per_wave == 2 || t.qsgd_buckets_per_wave == 4);
+            t.qsgd_buckets_per_wave == 2 || t.qsgd_buckets_per_wave == 4) &&
+           (t.dq_words_per_thread == 1 || t.dq_words_per_thread == 2);
 }
 
 void set_tuning(const gcq_tuning &t)

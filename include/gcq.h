@@ -453,23 +453,29 @@ typedef struct gcq_tuning {
                                wavefront takes at once, one per group of 64/H
                                lanes: 1, 2 or 4, limited to d H <= 1024; 0:
                                H = 1024/d for d <= 1024, else 1 (default) */
+    int dq_words_per_thread; /* gc2_dequant_reduce: packed words per thread,
+                               1 or 2 (default: 8-byte loads, used when every
+                               worker array is 8-byte aligned, else 1) */
 } gcq_tuning;
 
 /*
  * gcq_get_tuning -- copy the current knobs into *out (host struct).  The
  * initial values are the library defaults, overridden by the environment
- * variables GCQ_GC2_LAYOUT, GCQ_GC2_NT, GCQ_GC2_BLOCKS_PER_CU,
+ * variables GCQ_GC2_UNROLL, GCQ_GC2_NT, GCQ_GC2_BLOCKS_PER_CU,
  * GCQ_DQ_NT_LOADS, GCQ_DQ_NT_STORES, GCQ_DQ_LDS_STORES, GCQ_DQ_FP4_DECODE,
- * GCQ_DQ_BLOCKS_PER_CU, GCQ_QSGD_NT, GCQ_QSGD_RCP and GCQ_QSGD_DEQUANT_NT when
- * set.
+ * GCQ_DQ_BLOCKS_PER_CU, GCQ_DQ_WORDS_PER_THREAD, GCQ_QSGD_NT, GCQ_QSGD_RCP,
+ * GCQ_QSGD_DEQUANT_NT, GCQ_QSGD_BLOCKS_PER_CU, GCQ_QSGD_DEQUANT_BLOCKS_PER_CU
+ * and GCQ_QSGD_BUCKETS_PER_WAVE when set (block counts and gc2_nt are
+ * clamped into range, a flag reads any nonzero value as 1, and any other
+ * invalid value takes the default).
  * Errors: GCQ_ERR_NULL.
  *
  * gcq_set_tuning -- replace the knobs with *t (host struct).  Takes effect
  * for calls made after it returns; it must not run concurrently with
  * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
  * flag not 0/1, gc2_nt outside 0..15, gc2_unroll not 1/2/4, a block
- * count outside 0..1024); on error
- * nothing changes.
+ * count outside 0..1024, qsgd_buckets_per_wave not 0/1/2/4,
+ * dq_words_per_thread not 1/2); on error nothing changes.
  */
 int gcq_get_tuning(gcq_tuning *out);
 int gcq_set_tuning(const gcq_tuning *t);

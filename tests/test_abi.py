@@ -262,7 +262,8 @@ def test_tuning_roundtrip_and_validation(lib):
                        ("gc2_blocks_per_cu", 1025), ("dq_blocks_per_cu", -3), ("qsgd_nt", 7),
                        ("qsgd_rcp", 2), ("qsgd_dequant_nt", 3), ("dq_fp4_decode", 2),
                        ("qsgd_blocks_per_cu", -1), ("qsgd_dequant_blocks_per_cu", 1025),
-                       ("qsgd_buckets_per_wave", 3), ("qsgd_buckets_per_wave", -1)]:
+                       ("qsgd_buckets_per_wave", 3), ("qsgd_buckets_per_wave", -1),
+                       ("dq_words_per_thread", 3), ("dq_words_per_thread", 0)]:
         b = gcq.Tuning(**saved)
         setattr(b, field, bad)
         assert lib.gcq_set_tuning(ctypes.byref(b)) == E_PARAM, field

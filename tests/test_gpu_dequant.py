@@ -44,10 +44,13 @@ def test_config3_w16(gpu):
 
 
 DQ_VARIANTS = [dict(dq_nt_loads=l, dq_nt_stores=s, dq_lds_stores=d, dq_blocks_per_cu=b,
-                    dq_fp4_decode=f)
-               for (l, s, d, b, f) in [(1, 1, 1, 0, 1), (1, 0, 0, 0, 1), (0, 1, 1, 4, 0),
-                                       (0, 0, 0, 2, 1), (1, 1, 0, 0, 0), (0, 0, 1, 1, 1),
-                                       (1, 1, 1, 8, 0), (0, 1, 0, 0, 1)]]
+                    dq_fp4_decode=f, dq_words_per_thread=k)
+               for (l, s, d, b, f, k) in [(1, 1, 1, 0, 1, 1), (1, 0, 0, 0, 1, 1),
+                                          (0, 1, 1, 4, 0, 1), (0, 0, 0, 2, 1, 1),
+                                          (1, 1, 0, 0, 0, 1), (0, 0, 1, 1, 1, 1),
+                                          (1, 1, 1, 8, 0, 1), (0, 1, 0, 0, 1, 1),
+                                          (1, 1, 1, 0, 1, 2), (0, 0, 1, 3, 0, 2),
+                                          (1, 0, 1, 0, 1, 2), (0, 1, 1, 0, 0, 2)]]
 
 
 @pytest.mark.parametrize("var", range(len(DQ_VARIANTS)))
