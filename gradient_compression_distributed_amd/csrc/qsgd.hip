@@ -561,8 +561,9 @@ constexpr uint32_t kAvgWorkerBytes = kAvgSlots * 64u;
 // register, and the worker's place in the group is the LDS instruction's
 // immediate offset.  The empty asm keeps the compiler from folding the
 // byte extraction back into a shift-and-mask per element.  All eight table
-// reads are issued before the additions.
-template <uint32_t J>
+// reads are issued before the additions.  Uni: the word's eight elements
+// share one bucket (d a multiple of 8), and off[0] is every element's row.
+template <uint32_t J, bool Uni>
 __device__ __forceinline__ void avg_word(float (&a)[8], uint32_t w, const char *tb,
                                          const uint32_t (&off)[8])
 {
@@ -574,7 +575,7 @@ __device__ __forceinline__ void avg_word(float (&a)[8], uint32_t w, const char *
     for (int e = 0; e < 8; ++e) {
         const uint32_t src = (e & 1) ? lo : hi;
         const uint32_t byte = (src >> (8 * (3 - e / 2))) & 0xFFu;
-        t[e] = *(const float *)(tb + (off[e] + byte) + J * kAvgWorkerBytes);
+        t[e] = *(const float *)(tb + (off[Uni ? 0 : e] + byte) + J * kAvgWorkerBytes);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -582,17 +583,17 @@ __device__ __forceinline__ void avg_word(float (&a)[8], uint32_t w, const char *
 }
 
 // Workers l .. l+N-1 (their words w[0..N-1] already loaded), in order.
-template <uint32_t N, uint32_t J = 0>
+template <uint32_t N, bool Uni, uint32_t J = 0>
 __device__ __forceinline__ void avg_words(float (&a)[8], const uint32_t (&w)[kAvgChunk],
                                           const char *tb, const uint32_t (&offc)[8])
 {
     if constexpr (J < N) {
-        avg_word<J>(a, w[J], tb, offc);
-        avg_words<N, J + 1>(a, w, tb, offc);
+        avg_word<J, Uni>(a, w[J], tb, offc);
+        avg_words<N, Uni, J + 1>(a, w, tb, offc);
     }
 }
 
-template <uint32_t N, bool NT>
+template <uint32_t N, bool NT, bool Uni>
 __device__ __forceinline__ void avg_group(float (&a)[8], uint32_t (&w)[kAvgChunk], bool loaded,
                                           const QsgdMsgs &ms, uint32_t l, uint64_t wi,
                                           const char *tb, const uint32_t (&off)[8])
@@ -604,14 +605,14 @@ __device__ __forceinline__ void avg_group(float (&a)[8], uint32_t (&w)[kAvgChunk
     }
     uint32_t offc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < (Uni ? 1 : 8); ++e) {
         offc[e] = off[e] + l * kAvgWorkerBytes;
         asm volatile("" : "+v"(offc[e]));   // one add per group, not per read
     }
-    avg_words<N>(a, w, tb, offc);
+    avg_words<N, Uni>(a, w, tb, offc);
 }
 
-template <bool Pow2K, bool NT>
+template <bool Pow2K, bool NT, bool Uni>
 __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms, uint32_t K,
                                                                       uint64_t n, uint32_t d,
                                                                       uint32_t s,
@@ -633,38 +634,48 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
         const uint64_t wi = (e_tile >> 3) + tid;
         const bool valid = wi < nwords;
         // the first group's nibble words do not depend on the table: their
-        // loads are issued before it is built (16 workers, or 8 for K < 16)
+        // loads are issued before it is built (16 workers, 8 for K < 16,
+        // all K for K < 8)
         uint32_t w[kAvgChunk];
-        const uint32_t first = K >= 16u ? 16u : (K >= 8u ? 8u : 0u);
-        if (valid && first) {
+        const uint32_t first = K >= 16u ? 16u : (K >= 8u ? 8u : K);
+        if (valid) {
+            if (first >= 8u) {
 #pragma unroll
-            for (uint32_t j = 0; j < 8; ++j)
-                w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
-            if (first == 16u) {
-#pragma unroll
-                for (uint32_t j = 8; j < 16; ++j)
+                for (uint32_t j = 0; j < 8; ++j)
                     w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
+                if (first == 16u) {
+#pragma unroll
+                    for (uint32_t j = 8; j < 16; ++j)
+                        w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
+                }
+            } else {
+#pragma unroll
+                for (uint32_t j = 0; j < 7; ++j)
+                    if (j < first)
+                        w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[j] + wi);
             }
         }
-        // thread (l, nib) = (tid / 16 + 16 j, tid % 16) fills nibble nib of
-        // worker l for every bucket of the tile; its scale loads are issued
-        // together
+        // thread (l, lev) = (tid / 8 + 32 j, tid % 8) fills level lev of
+        // worker l, both signs (nibbles lev and 8 | lev: one division), for
+        // every bucket of the tile; its scale loads are issued together.
+        // With K <= 16 the upper half of the workgroup has no entries.
         {
-            const uint32_t nib = tid & 15u;
-            const float lev = (float)(nib & 7u);
-            for (uint32_t l = tid >> 4; l < K; l += kBlockThreads / 16u) {
+            const uint32_t lev = tid & 7u;
+            const float levf = (float)lev;
+            for (uint32_t l = tid >> 3; l < K; l += kBlockThreads / 8u) {
                 const GCQ_GLOBAL float *sc = (const GCQ_GLOBAL float *)ms.scales[l] + b0;
                 float v[kAvgSlots];
 #pragma unroll
                 for (uint32_t bb = 0; bb < kAvgSlots; ++bb)
                     v[bb] = bb < nbk ? sc[bb] : 0.0f;
-                float *tl = table + l * (kAvgWorkerBytes / 4u) + nib;
+                float *tl = table + l * (kAvgWorkerBytes / 4u) + lev;
 #pragma unroll
                 for (uint32_t bb = 0; bb < kAvgSlots; ++bb) {
                     if (bb < nbk) {
-                        float m = v[bb] * lev;
+                        float m = v[bb] * levf;
                         m = m / sf;
-                        tl[16u * bb] = (nib & 8u) ? -m : m;
+                        tl[16u * bb] = m;
+                        tl[16u * bb + 8u] = -m;
                     }
                 }
             }
@@ -681,24 +692,39 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
             // reads stay inside the allocation and they are never stored.
             const uint32_t rel = (uint32_t)(wi * 8u - b0 * d);
             const uint32_t bb0 = rel / d;
-            const uint32_t brk = (bb0 + 1u) * d - rel;
+            const uint32_t brk = (bb0 + 1u) * d - rel;   // >= 8 when Uni
             uint32_t off[8];   // byte offset of each element's table row
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                off[e] = (bb0 + ((uint32_t)e >= brk ? 1u : 0u)) * 64u;
+                off[e] = (bb0 + (!Uni && (uint32_t)e >= brk ? 1u : 0u)) * 64u;
             const char *tb = (const char *)table;
-            // groups of 16, then 8 workers: every load issued, then decoded
+            // groups of 16, then 8 workers, then the last K mod 8 (uniform
+            // branches per word): every load of a group issued, then
+            // decoded in worker order
             uint32_t l = 0;
             for (; l + 16u <= K; l += 16u)
-                avg_group<16, NT>(a, w, l == 0, ms, l, wi, tb, off);
+                avg_group<16, NT, Uni>(a, w, l == 0, ms, l, wi, tb, off);
             for (; l + 8u <= K; l += 8u)
-                avg_group<8, NT>(a, w, l == 0, ms, l, wi, tb, off);
-            for (; l < K; ++l) {
+                avg_group<8, NT, Uni>(a, w, l == 0, ms, l, wi, tb, off);
+            const uint32_t rem = K - l;   // 0 .. 7, uniform
+            if (rem) {
+                if (l != 0) {
+#pragma unroll
+                    for (uint32_t j = 0; j < 7; ++j)
+                        if (j < rem)
+                            w[j] = ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l + j] + wi);
+                }
                 uint32_t offc[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < (Uni ? 1 : 8); ++e)
                     offc[e] = off[e] + l * kAvgWorkerBytes;
-                avg_word<0>(a, ld<NT>((const GCQ_GLOBAL uint32_t *)ms.nibbles[l] + wi), tb, offc);
+                if (rem > 0u) avg_word<0, Uni>(a, w[0], tb, offc);
+                if (rem > 1u) avg_word<1, Uni>(a, w[1], tb, offc);
+                if (rem > 2u) avg_word<2, Uni>(a, w[2], tb, offc);
+                if (rem > 3u) avg_word<3, Uni>(a, w[3], tb, offc);
+                if (rem > 4u) avg_word<4, Uni>(a, w[4], tb, offc);
+                if (rem > 5u) avg_word<5, Uni>(a, w[5], tb, offc);
+                if (rem > 6u) avg_word<6, Uni>(a, w[6], tb, offc);
             }
         }
         float o[8];
@@ -908,20 +934,30 @@ hipError_t launch_qsgd_average(const QsgdMsgs &ms, uint32_t K, uint64_t n, uint3
     if (slots <= kAvgSlots && d <= (1u << 30) && lds <= 64u * 1024u) {
         const uint64_t ntiles = (n + kAvgTileElems - 1) / kAvgTileElems;
         const uint32_t grid = grid_for(ntiles, tu.qsgd_dequant_blocks_per_cu);
-#define GCQ_AVG(P, NT)                                                                        \
-    qsgd_average_kernel<P, NT><<<grid, kBlockThreads, (size_t)lds, stream>>>(                 \
+        // a nibble word never straddles a bucket boundary when 8 divides d
+        const bool uni = (d & 7u) == 0u;
+#define GCQ_AVG(P, NT, U)                                                                     \
+    qsgd_average_kernel<P, NT, U><<<grid, kBlockThreads, (size_t)lds, stream>>>(              \
         ms, K, n, d, s, kf, ntiles, out)
+#define GCQ_AVG_U(P, NT)                                                                      \
+    do {                                                                                      \
+        if (uni)                                                                              \
+            GCQ_AVG(P, NT, true);                                                             \
+        else                                                                                  \
+            GCQ_AVG(P, NT, false);                                                            \
+    } while (0)
         if (pow2) {
             if (tu.qsgd_dequant_nt)
-                GCQ_AVG(true, true);
+                GCQ_AVG_U(true, true);
             else
-                GCQ_AVG(true, false);
+                GCQ_AVG_U(true, false);
         } else {
             if (tu.qsgd_dequant_nt)
-                GCQ_AVG(false, true);
+                GCQ_AVG_U(false, true);
             else
-                GCQ_AVG(false, false);
+                GCQ_AVG_U(false, false);
         }
+#undef GCQ_AVG_U
 #undef GCQ_AVG
     } else {
         const uint32_t grid = grid_for((n + kBlockThreads - 1) / kBlockThreads, 0);

@@ -126,7 +126,7 @@ def check_average(gpu, scales, nibs, n, d, s):
     return out
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 9, 16, 24, 31, 64])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 22, 24, 31, 64])
 def test_average_workers(knobs, K):
     gpu = knobs
     say("qsgd average K", K)
