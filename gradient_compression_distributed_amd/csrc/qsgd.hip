@@ -34,14 +34,15 @@ __device__ __forceinline__ void uniforms4(uint64_t q, uint32_t k0, uint32_t k1, 
         u[j] = (float)(c[j] >> 8) * 0x1p-24f;
 }
 
-// The same draws as integers U = u 2^24 (exact floats below 2^24).
-__device__ __forceinline__ void uniforms4_int(uint64_t q, uint32_t k0, uint32_t k1, float (&U)[4])
+// The four raw output words behind those uniforms (u = (c >> 8) 2^-24).
+__device__ __forceinline__ void philox_words4(uint64_t q, uint32_t k0, uint32_t k1,
+                                              uint32_t (&c)[4])
 {
-    uint32_t c[4] = {(uint32_t)q, (uint32_t)(q >> 32), 0u, 0u};
+    c[0] = (uint32_t)q;
+    c[1] = (uint32_t)(q >> 32);
+    c[2] = 0u;
+    c[3] = 0u;
     philox4x32_10(c, k0, k1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        U[j] = (float)(c[j] >> 8);
 }
 
 // Level of one element (Knowl 1), exactly as defined: a = |g|/norm (one
@@ -66,32 +67,42 @@ __device__ __forceinline__ uint32_t qsgd_level_exact(float gabs, float norm, flo
 
 // The same level without a division per element.  With l = floor(x) and
 // p = x - l, the level l + [u < p] equals ceil(x - u) in exact arithmetic
-// (u in [0, 1); the integer case x - u = l is p = u, level l).  The kernel
-// computes d = RN(x' - u) with x' = RN(|g| * rs), rs = RN(RN(1/norm) * s),
-// and u = U 2^-24 folded into one fma.  For a bucket norm in
-// [2^-120, 2^120], x' differs from the exact x = RN(RN(|g|/norm) * s) by
-// less than 40 * 2^-24 (five relative roundings of at most 2^-24 each on a
-// value below 7.0001, since |g| <= norm up to its own rounding), and the
-// subtraction adds at most 2^-22 (half an ulp below 8): |d - (x - u)| <
-// 44 * 2^-24 < kGuard = 2^-18.  So whenever d lies more than kGuard from
-// every integer, ceil(d) = ceil(x - u), the exact level.  That covers the
-// clamp at s too: x <= s (1 + 3 * 2^-24), so x - u lies within kGuard of s
-// or below s - kGuard whenever x >= s, and ceil gives s or the lane falls
-// back.  The shortcut only runs for finite buckets (a NaN or Inf element
-// makes the norm NaN or Inf, outside the range), so d is finite.
+// (u in [0, 1); the integer case x - u = l is p = u, level l).  With
+// T = x + 1 - u > 0 that is trunc(T) whenever T is not an integer.  The
+// clamp needs no case of its own: |g| <= norm for the L2 norm (the float64
+// sum of squares and its square root only round towards values >= g^2 and
+// |g|) and for the largest magnitude, so a = RN(|g|/norm) <= 1 and x <= s;
+// x = s gives T in (s, s + 1], whose trunc is s unless T = s + 1 (u = 0),
+// an integer.
+//
+// The kernel computes d1 = RN(t - U' 2^-32) with t = RN(|g| rs + 1) (one
+// fma), rs = RN(RN(1/norm) s), and U' = RN(c) the raw 32-bit Philox word
+// converted to float (no shift).  For a bucket norm in [2^-120, 2^120]:
+//   |g| rs is within 4 relative roundings of x (two on each side, on a value
+//     below 7.0001): 28 * 2^-24;
+//   t rounds |g| rs + 1 < 9 once: at most 2^-21 = 8 * 2^-24;
+//   U' 2^-32 is within 2^-24 (the 8 dropped bits) + 2^-25 (the conversion)
+//     of u = (c >> 8) 2^-24: 1.5 * 2^-24;
+//   the fma rounds t - U' 2^-32 < 9 once: 8 * 2^-24;
+// so |d1 - T| < 46 * 2^-24 < kGuard = 2^-18.  Whenever d1 lies more than
+// kGuard from every integer, trunc(d1) = trunc(T), the exact level (and d1
+// then stays below s + 1 - kGuard, so the level fits its 3 bits).  The
+// shortcut only runs for finite buckets (a NaN or Inf element makes the
+// norm NaN or Inf, outside the range), so d1 is finite and d1 >= 0.
 constexpr float kGuard = 0x1p-18f;
-// kGuard < f < 1 - kGuard for f = ceil(d) - d, as one comparison of
-// |f - 0.5|; its rounding is monotone and 0.5 - kGuard is a float, so it
-// only ever errs towards "unsafe".
+// kGuard < f < 1 - kGuard for f = fract(d1) (exact for d1 in [0, 9)), as
+// one comparison of |f - 0.5|; its rounding is monotone and 0.5 - kGuard is
+// a float, so it only ever errs towards "unsafe".
 constexpr float kSafeDist = 0.5f - kGuard;
 
-// Level from the shortcut; `dist` = |f - 0.5|, safe when below kSafeDist.
-__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, float U, float &dist)
+// Level from the shortcut; `dist` = |fract(d1) - 0.5|, safe when below
+// kSafeDist (an unsafe lane's return value is not used).
+__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, uint32_t c, float &dist)
 {
-    const float d = __builtin_fmaf(U, -0x1p-24f, gabs * rs);
-    const float c = __builtin_ceilf(d);
-    dist = __builtin_fabsf((c - d) - 0.5f);
-    return (uint32_t)c;                      // c in [-0, s + 1]: in range
+    const float t = __builtin_fmaf(gabs, rs, 1.0f);
+    const float d1 = __builtin_fmaf((float)c, -0x1p-32f, t);
+    dist = __builtin_fabsf(__builtin_amdgcn_fractf(d1) - 0.5f);
+    return (uint32_t)d1;                     // d1 in [0, s + 2): in range
 }
 
 __device__ __forceinline__ uint32_t sign_bit(float gv) { return gv < 0.0f ? 8u : 0u; }
@@ -253,15 +264,15 @@ __global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float gq[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-            float U[4];
-            uniforms4_int((base + CH * r + 4u * l) >> 2, k0, k1, U);
+            uint32_t cw[4];
+            philox_words4((base + CH * r + 4u * l) >> 2, k0, k1, cw);
             uint32_t lv[4];
             bool all_ok = false;
             if (fast) {
                 float dist[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[q], dist[q]);
+                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist[q]);
                 all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
             }
             if (all_ok) {
@@ -273,9 +284,10 @@ __global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
                 for (int q = 0; q < 4; ++q) {
                     float dist = 1.0f;
                     if (fast)
-                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, U[q], dist);
+                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist);
                     if (!(dist < kSafeDist))
-                        lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s, U[q] * 0x1p-24f);
+                        lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s,
+                                                 (float)(cw[q] >> 8) * 0x1p-24f);
                 }
                 h[r] = pack4_exact(gq, lv);
             }
