@@ -53,6 +53,21 @@ KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gc2_quantize.hip", "gcq_device.h
                                                "gcq_internal.h")]
 
 
+def arena(layout, dev):
+    """Views of one device allocation, one per (numel, dtype) in `layout`,
+    each starting on a 4 KiB boundary."""
+    import torch
+
+    offs, total = [], 0
+    for numel, dt in layout:
+        offs.append(total)
+        nbytes = numel * torch.tensor([], dtype=dt).element_size()
+        total += (nbytes + 4095) // 4096 * 4096
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    return [buf[o:o + numel * torch.tensor([], dtype=dt).element_size()].view(dt)
+            for o, (numel, dt) in zip(offs, layout)]
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
@@ -115,19 +130,26 @@ def main():
     K, Wm = args.steps, args.warmup
 
     # ---------------------------------------------------------- setup (untimed)
+    # Every buffer of the step is a view into one device allocation, as a
+    # flat data-parallel gradient buffer would be.  (With one allocation per
+    # 4 GiB buffer, one of the four gradient buffers ran the quantizer about
+    # 6% slower than the others, on every box tried.)
     ngrad = min(K + Wm, 4)
-    grads = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(ngrad)]
+    nw = n // 16
+    layout = ([(n, torch.float32)] * ngrad + [(n, torch.float32)] +
+              [(nw, torch.int32)] * W_WORKERS + [(n, torch.float32)] +
+              [(gcq.qsgd_num_buckets(n, QSGD_D), torch.float32),
+               (gcq.qsgd_nibble_words(n), torch.int32), (n, torch.float32)])
+    views = arena(layout, dev)
+    grads = views[:ngrad]
+    r = views[ngrad]
+    words = views[ngrad + 1:ngrad + 1 + W_WORKERS]
+    acc, norms, nib, qout = views[ngrad + 1 + W_WORKERS:]
     for i, g in enumerate(grads):
         wl.fill_bucketed_normal_(g, cfg, i)
-    r = torch.zeros(n, dtype=torch.float32, device=dev)
-    nw = n // 16
-    words = [torch.empty(nw, dtype=torch.int32, device=dev) for _ in range(W_WORKERS)]
+    r.zero_()
     for w in range(1, W_WORKERS):
         wl.fill_iid_field_words_(words[w], cfg.cid, w)
-    acc = torch.empty(n, dtype=torch.float32, device=dev)
-    norms = torch.empty(gcq.qsgd_num_buckets(n, QSGD_D), dtype=torch.float32, device=dev)
-    nib = torch.empty(gcq.qsgd_nibble_words(n), dtype=torch.int32, device=dev)
-    qout = torch.empty(n, dtype=torch.float32, device=dev)
     wpb = blk // 16
     blists = [gcq.BucketList([(g[b * blk:(b + 1) * blk], r[b * blk:(b + 1) * blk],
                                words[0][b * wpb:(b + 1) * wpb], cfg.t) for b in range(nb)])
