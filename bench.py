@@ -113,7 +113,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
               "supported: the W workers of the reduce are simulated buffers on one GPU and "
-              "this build runs no collectives.", file=sys.stderr, flush=True)
+              "the library runs no collectives.", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import numpy as np
@@ -125,7 +125,7 @@ def main():
     gcq.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = wl.CONFIGS[5]
+    cfg = wl.FUSED_1G
     n, nb, blk = cfg.n, cfg.n // cfg.block, cfg.block
     K, Wm = args.steps, args.warmup
 
@@ -149,7 +149,7 @@ def main():
         wl.fill_bucketed_normal_(g, cfg, i)
     r.zero_()
     for w in range(1, W_WORKERS):
-        wl.fill_iid_field_words_(words[w], cfg.cid, w)
+        wl.fill_iid_field_words_(words[w], cfg.stream, w)
     wpb = blk // 16
     blists = [gcq.BucketList([(g[b * blk:(b + 1) * blk], r[b * blk:(b + 1) * blk],
                                words[0][b * wpb:(b + 1) * wpb], cfg.t) for b in range(nb)])
@@ -224,9 +224,9 @@ def main():
     # and the update plus the single-buffer quantizer as two launches
     next_ops = None
     if not args.no_next:
-        cfg7 = wl.CONFIGS[7]
+        cds = wl.CDSGD_1G
         g, wloc = grads[0], qout
-        wl.fill_normal_(wloc, cfg7.cid, 999, cfg7.w_sigma)
+        wl.fill_normal_(wloc, cds.stream, 999, cds.w_sigma)
         reps = max(3, K // 2)
 
         def timed(fn):
@@ -239,10 +239,10 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        fused_ms = timed(lambda: gcq.cdsgd_update_quantize(g, r, wloc, cfg7.t, cfg7.eta,
+        fused_ms = timed(lambda: gcq.cdsgd_update_quantize(g, r, wloc, cds.t, cds.eta,
                                                            out=words[0]))
-        upd_ms = timed(lambda: gcq.cdsgd_local_update(g, wloc, cfg7.eta))
-        quant_ms = timed(lambda: gcq.gc2_quantize(g, r, cfg7.t, out=words[0]))
+        upd_ms = timed(lambda: gcq.cdsgd_local_update(g, wloc, cds.eta))
+        quant_ms = timed(lambda: gcq.gc2_quantize(g, r, cds.t, out=words[0]))
         next_ops = {}
         for name, ms, bpe in (("cdsgd_update_quantize", fused_ms, 20.25),
                               ("cdsgd_local_update", upd_ms, 12.0)):
@@ -251,7 +251,7 @@ def main():
                               "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                               "bytes_per_element": bpe}
         next_ops["cdsgd_update_quantize"]["separate_launches_ms"] = round(upd_ms + quant_ms, 4)
-        next_ops["cdsgd_update_quantize"]["config"] = {"eta": cfg7.eta, "t": cfg7.t, "n": n}
+        next_ops["cdsgd_update_quantize"]["config"] = {"eta": cds.eta, "t": cds.t, "n": n}
 
         # QSGD with max-norm bucket scales, and the 16-worker decode-average
         mx_ms = timed(lambda: gcq.qsgd_quantize_maxnorm(g, QSGD_D, QSGD_S, wl.qsgd_seed(7),
@@ -396,7 +396,7 @@ def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
     # same gradient (inputs that are another row's output are made untimed)
     m = 1 << 21
     gs = g_dev[:m].cpu().numpy()
-    cfg7 = wl.CONFIGS[7]
+    cds = wl.CDSGD_1G
     rs = np.random.default_rng(7)
     nxt = {}
 
@@ -405,10 +405,10 @@ def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
         fn()
         return m / (time.perf_counter() - t0)
 
-    rr, ww = np.zeros(m, np.float32), (rs.standard_normal(m) * cfg7.w_sigma).astype(np.float32)
-    nxt["cdsgd_update_quantize"] = rate(lambda: oracle.cdsgd_update_quantize(gs, rr, ww, cfg7.t,
-                                                                             cfg7.eta))
-    nxt["cdsgd_local_update"] = rate(lambda: oracle.cdsgd_local_update(gs, ww, cfg7.eta))
+    rr, ww = np.zeros(m, np.float32), (rs.standard_normal(m) * cds.w_sigma).astype(np.float32)
+    nxt["cdsgd_update_quantize"] = rate(lambda: oracle.cdsgd_update_quantize(gs, rr, ww, cds.t,
+                                                                             cds.eta))
+    nxt["cdsgd_local_update"] = rate(lambda: oracle.cdsgd_local_update(gs, ww, cds.eta))
     nxt["qsgd_quantize_maxnorm"] = rate(lambda: oracle.qsgd_quantize_maxnorm(gs, QSGD_D, QSGD_S,
                                                                              wl.qsgd_seed(7)))
     msgs = [oracle.qsgd_quantize(gs, QSGD_D, QSGD_S, wl.qsgd_seed(200 + k)) for k in range(W_WORKERS)]

@@ -33,9 +33,9 @@ def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-def test_config3_w16(gpu):
-    cfg = wl.CONFIGS[3]
-    say("dequant config 3", cfg.n, cfg.workers)
+def test_w16_resnet50_sized(gpu):
+    cfg = wl.REDUCE_W16_RESNET50
+    say("dequant W = 16 ResNet-50-sized", cfg.n, cfg.workers)
     nw = oracle.packed_words(cfg.n)
     ws = [wl.worker_words(cfg, w, nw) for w in range(cfg.workers)]
     acc_d = gpu.gc2_dequant_reduce([dev(w) for w in ws], cfg.n, cfg.t)

@@ -135,7 +135,7 @@ def test_full_size_sampled(gpu):
 
     n, d, s = 1 << 30, 512, 7
     say("elias full size", n)
-    cfg = wl.CONFIGS[5]
+    cfg = wl.FUSED_1G
     g = torch.empty(n, device="cuda")
     wl.fill_bucketed_normal_(g, cfg, 0)
     norms, nib = gpu.qsgd_quantize(g, d, s, wl.qsgd_seed(3))

@@ -51,9 +51,9 @@ def default_tuning(gpu):
     gpu.set_tuning(**old)
 
 
-def test_config1_three_steps(gpu):
-    cfg = wl.CONFIGS[1]
-    say("gc2 config 1", cfg.n)
+def test_ragged_65k_three_steps(gpu):
+    cfg = wl.GC2_RAGGED_65K
+    say("gc2 ragged 65,541", cfg.n)
     r_h = np.zeros(cfg.n, np.float32)
     r_d = dev(r_h.copy())
     for step in range(cfg.steps):
@@ -65,9 +65,9 @@ def test_config1_three_steps(gpu):
         assert np.array_equal(bits(host(r_d)), bits(r_h)), step
 
 
-def test_config2_ten_steps(gpu):
-    cfg = wl.CONFIGS[2]
-    say("gc2 config 2", cfg.n)
+def test_resnet50_ten_steps(gpu):
+    cfg = wl.GC2_RESNET50
+    say("gc2 ResNet-50-sized", cfg.n)
     r_h = np.zeros(cfg.n, np.float32)
     r_d = dev(r_h.copy())
     for step in range(cfg.steps):
@@ -139,7 +139,7 @@ def test_resume_from_host_copy(gpu):
     import torch
 
     say("gc2 resume")
-    cfg = wl.CONFIGS[1]
+    cfg = wl.GC2_RAGGED_65K
     r1 = torch.zeros(cfg.n, device="cuda")
     outs = [gpu.gc2_quantize(dev(wl.gradient(cfg, s)), r1, cfg.t) for s in range(3)]
     r2 = torch.zeros(cfg.n, device="cuda")
@@ -363,15 +363,15 @@ def _code_properties(w32, r_new, v, t):
     assert bool((r_new[z].abs() < t).all())
 
 
-def test_config5_full_size_fused(gpu):
+def test_1g_full_size_fused(gpu):
     """1G elements, 128 fusion buckets, the fused launch the benchmark times:
     sampled buckets bit-exact against the oracle over two steps (the oracle
     chains its own residual), fused == per-bucket launches on every bucket,
     and the per-code facts on every element."""
     import torch
 
-    cfg = wl.CONFIGS[5]
-    say("gc2 config 5 full size", cfg.n)
+    cfg = wl.FUSED_1G
+    say("gc2 2^30 fused full size", cfg.n)
     nb = cfg.n // cfg.block
     g = torch.empty(cfg.n, device="cuda")
     r = torch.zeros(cfg.n, device="cuda")

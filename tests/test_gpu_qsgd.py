@@ -65,12 +65,12 @@ def knobs(gpu):
 
 @pytest.mark.parametrize("rcp,nt,dnt,bpc,dbpc", [(1, 0, 1, 8, 0), (0, 1, 0, 0, 3),
                                                   (1, 1, 0, 1, 8), (1, 0, 1, 0, 0)])
-def test_config4(knobs, rcp, nt, dnt, bpc, dbpc):
+def test_alexnet_sized(knobs, rcp, nt, dnt, bpc, dbpc):
     gpu = knobs
     gpu.set_tuning(qsgd_rcp=rcp, qsgd_nt=nt, qsgd_dequant_nt=dnt, qsgd_blocks_per_cu=bpc,
                    qsgd_dequant_blocks_per_cu=dbpc)
-    cfg = wl.CONFIGS[4]
-    say("qsgd config 4", cfg.n, "rcp", rcp, "nt", nt, "blocks/CU", bpc, dbpc)
+    cfg = wl.QSGD_ALEXNET
+    say("qsgd AlexNet-sized", cfg.n, "rcp", rcp, "nt", nt, "blocks/CU", bpc, dbpc)
     g = wl.gradient(cfg, 0)
     norms, nib, out, want_norms, want_out = check_case(gpu, g, cfg.d, cfg.s, wl.qsgd_seed(0))
     assert norms.size == 119_338 and nib.size == 7_637_605
@@ -231,7 +231,7 @@ def test_full_size_1g_sampled(gpu):
     their global indices, dequant)."""
     import torch
 
-    cfg = wl.CONFIGS[5]
+    cfg = wl.FUSED_1G
     say("qsgd 1G")
     g = torch.empty(cfg.n, device="cuda")
     wl.fill_bucketed_normal_(g, cfg, 0)

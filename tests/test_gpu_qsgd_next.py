@@ -57,11 +57,11 @@ def check_maxnorm(gpu, g, d, s, seed):
 
 # ---------------------------------------------------------------- max-norm
 @pytest.mark.parametrize("rcp,bpc", [(1, 32), (0, 0), (1, 0)])
-def test_maxnorm_config4(knobs, rcp, bpc):
+def test_maxnorm_alexnet_sized(knobs, rcp, bpc):
     gpu = knobs
     gpu.set_tuning(qsgd_rcp=rcp, qsgd_blocks_per_cu=bpc)
-    cfg = wl.CONFIGS[4]
-    say("qsgd max-norm config 4", cfg.n, "rcp", rcp, "blocks/CU", bpc)
+    cfg = wl.QSGD_ALEXNET
+    say("qsgd max-norm AlexNet-sized", cfg.n, "rcp", rcp, "blocks/CU", bpc)
     check_maxnorm(gpu, wl.gradient(cfg, 0), cfg.d, cfg.s, wl.qsgd_seed(0))
 
 
@@ -178,7 +178,7 @@ def test_average_full_size_sampled(gpu):
 
     K, n, d, s = 16, 1 << 30, 512, 7
     say("qsgd average full size", n, "K", K)
-    cfg = wl.CONFIGS[5]
+    cfg = wl.FUSED_1G
     g = torch.empty(n, device="cuda")
     wl.fill_bucketed_normal_(g, cfg, 0)
     scales, nibs = [], []

@@ -81,7 +81,7 @@ def test_code_01_reads_as_zero():
 
 def test_roundtrip_with_quantizer():
     # one worker: dequant(quantize(g + r)) + r_new == g + r up to roundings
-    cfg = wl.CONFIGS[1]
+    cfg = wl.GC2_RAGGED_65K
     g = wl.gradient(cfg, 0)
     r = np.zeros(cfg.n, np.float32)
     words = oracle.gc2_quantize(g, r, cfg.t)
@@ -91,8 +91,8 @@ def test_roundtrip_with_quantizer():
     assert np.all(np.abs(acc.astype(np.float64) + r - g) <= bound)
 
 
-def test_config3_inputs_have_the_stated_mix():
-    cfg = wl.CONFIGS[3]
+def test_reduce_inputs_have_the_stated_mix():
+    cfg = wl.REDUCE_W16_RESNET50
     w = wl.worker_words(cfg, 0, 200_000)
     fields = (w[:, None] >> (2 * np.arange(16, dtype=np.uint32))[None, :]) & 3
     frac = np.bincount(fields.ravel(), minlength=4) / fields.size

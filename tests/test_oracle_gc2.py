@@ -143,8 +143,8 @@ def _check_step_invariants(g, r_old, r_new, words, t):
         assert int(words[-1]) & ((1 << (32 - 2 * tail)) - 1) == 0
 
 
-def test_invariants_config1_three_steps():
-    cfg = wl.CONFIGS[1]
+def test_invariants_ragged_65k_three_steps():
+    cfg = wl.GC2_RAGGED_65K
     r = np.zeros(cfg.n, np.float32)
     for step in range(cfg.steps):
         g = wl.gradient(cfg, step)
@@ -154,8 +154,8 @@ def test_invariants_config1_three_steps():
         _check_step_invariants(g, r_old, r, words, cfg.t)
 
 
-def test_invariants_config2_blocks():
-    cfg = wl.CONFIGS[2]
+def test_invariants_resnet50_blocks():
+    cfg = wl.GC2_RESNET50
     sig = wl.block_sigmas(cfg)
     assert len(sig) == 25 and np.all((sig >= 1e-4) & (sig <= 1e-1))
     for b in (0, int(np.argmin(sig)), int(np.argmax(sig)), 24):
@@ -204,7 +204,7 @@ def test_ieee_special_values():
 
 def test_residual_carries_over_and_resumes():
     # the residual is the only state; resuming from a copy is identical
-    cfg = wl.CONFIGS[1]
+    cfg = wl.GC2_RAGGED_65K
     r = np.zeros(cfg.n, np.float32)
     outs = []
     for step in range(3):
