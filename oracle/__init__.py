@@ -287,10 +287,12 @@ def qsgd_dequant_average(scales: list, nibbles: list, n: int, d: int, s: int) ->
     return out
 
 
-def saps_keep(seed: int, n: int, c: float) -> np.ndarray:
-    """The mask: keep[i] for i < n (a bool array; one oracle call each)."""
+def saps_keep(seed: int, n: int, c: float, start: int = 0) -> np.ndarray:
+    """The mask: keep[i] for start <= i < start + n (a bool array; one
+    oracle call each)."""
     lib = _load()
-    return np.array([bool(lib.oracle_saps_keep(seed, i, ctypes.c_float(c))) for i in range(n)])
+    return np.array([bool(lib.oracle_saps_keep(seed, i, ctypes.c_float(c)))
+                     for i in range(start, start + n)], dtype=bool)
 
 
 def saps_gather(x: np.ndarray, c: float, seed: int) -> np.ndarray:
