@@ -275,22 +275,21 @@ __global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
                     lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist[q]);
                 all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
             }
-            if (all_ok) {
-                h[r] = pack4(gq, lv);
-            } else {
-                // rare: redo the group element by element, the exact way
-                // where the shortcut cannot decide
+            if (!all_ok) {
+                // rare: the exact level where the shortcut cannot decide
+                // (its test redone here, so the fast path keeps nothing)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    float dist = 1.0f;
+                    float dq = 1.0f;
                     if (fast)
-                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist);
-                    if (!(dist < kSafeDist))
+                        (void)qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dq);
+                    if (!(dq < kSafeDist))
                         lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s,
                                                  (float)(cw[q] >> 8) * 0x1p-24f);
                 }
-                h[r] = pack4_exact(gq, lv);
             }
+            // a fast bucket holds no NaN, so its signs may come from the bits
+            h[r] = fast ? pack4(gq, lv) : pack4_exact(gq, lv);
         }
         uint32_t *out = nib + (base >> 3) + (l >> 1);
         const bool odd = (lane & 1u) != 0;
