@@ -47,6 +47,20 @@ constexpr int kQuadBcast2 = 0xAA;  // quad_perm [2,2,2,2]
 constexpr int kQuadBcast3 = 0xFF;  // quad_perm [3,3,3,3]
 constexpr int kSwapPairs = 0xB1;   // quad_perm [1,0,3,2]
 
+// Block -> tile for a grid of exactly one block per tile (G blocks).  The
+// dispatcher hands consecutive workgroups to the 8 XCDs in turn, and each
+// XCD has its own L2; this gives XCD x the contiguous run of tiles
+// [x q + min(x, r), +q + [x < r]) (q = G / 8, r = G mod 8), so neighbouring
+// tiles share their L2 lines (e.g. the bucket scales several tiles read).
+// It is a bijection of [0, G) for any G, whatever the dispatch order.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint64_t xcd_tile(uint32_t b, uint32_t G)
+{
+    const uint32_t x = b % kXcds, i = b / kXcds, q = G / kXcds, r = G % kXcds;
+    return (uint64_t)x * q + (x < r ? x : r) + i;
+}
+
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64-bit products; the high halves are xored with the other counter
 // words and the round key, the words permuted; the key advances by the

@@ -636,7 +636,10 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const float sf = (float)s;
     const uint64_t nwords = (n + 7) >> 3;
-    for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    // one block per tile (the default): XCD-contiguous runs of tiles, so the
+    // scale lines a run of tiles shares are fetched into one L2
+    const uint64_t first = gridDim.x == ntiles ? dev::xcd_tile(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint64_t tile = first; tile < ntiles; tile += gridDim.x) {
         const uint64_t e_tile = tile * kAvgTileElems;
         const uint64_t e_end = e_tile + kAvgTileElems < n ? e_tile + kAvgTileElems : n;
         const uint64_t b0 = e_tile / d;
