@@ -6,8 +6,11 @@
 // Three steps over tiles of 8192 elements (256 threads x 32 elements):
 //   mask   -- each thread draws its 32 uniforms (8 Philox calls, the QSGD
 //             quantizer's stream), keeps element i when U_i < T with
-//             T = ceil(2^24 / c) (exactly u_i c < 1), writes one 32-bit mask
-//             word (bit j = element 32w + j) and the tile's kept count;
+//             T = ceil(2^24 / c) (exactly u_i c < 1), tested on the raw
+//             32-bit word as c_i <= 256 T - 1 (U_i = c_i >> 8; T is in
+//             [1, 2^24] for c in [1, inf), so 256 T - 1 fits 32 bits),
+//             writes one 32-bit mask word (bit j = element 32w + j) and the
+//             tile's kept count;
 //   scan   -- the tile counts become exclusive offsets (and the total);
 //   apply  -- per tile, a block scan of the threads' popcounts gives each
 //             thread its first rank; it then gathers x at its set bits into
@@ -47,7 +50,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, uint32_t lan
     return x;
 }
 
-__global__ __launch_bounds__(kSapsThreads) void saps_mask_kernel(uint64_t n, uint32_t T,
+__global__ __launch_bounds__(kSapsThreads) void saps_mask_kernel(uint64_t n, uint32_t Tm,
                                                                   uint32_t k0, uint32_t k1,
                                                                   uint32_t *__restrict__ mask,
                                                                   uint64_t *__restrict__ offs,
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kSapsThreads) void saps_mask_kernel(uint64_t n, uin
                 philox4x32_10(c, k0, k1);
 #pragma unroll
                 for (uint32_t r = 0; r < 4; ++r)
-                    word |= ((c[r] >> 8) < T ? 1u : 0u) << (4 * j + r);
+                    word |= (c[r] <= Tm ? 1u : 0u) << (4 * j + r);
             }
             if (n - e0 < 32u)
                 word &= (1u << (uint32_t)(n - e0)) - 1u;   // elements past n are not kept
@@ -240,7 +243,8 @@ hipError_t launch_saps_mask(uint64_t n, float c, uint64_t seed, uint32_t *mask, 
     const uint64_t ntiles = (n + kSapsTileElems - 1) / kSapsTileElems;
     if (ntiles) {
         const uint32_t grid = grid_for(ntiles, 0);
-        saps_mask_kernel<<<grid, kSapsThreads, 0, stream>>>(n, saps_threshold(c), (uint32_t)seed,
+        const uint32_t Tm = (uint32_t)(256u * (uint64_t)saps_threshold(c) - 1u);
+        saps_mask_kernel<<<grid, kSapsThreads, 0, stream>>>(n, Tm, (uint32_t)seed,
                                                             (uint32_t)(seed >> 32), mask, offs,
                                                             ntiles);
         const hipError_t e = hipGetLastError();
