@@ -623,8 +623,12 @@ __device__ __forceinline__ void avg_group(float (&a)[8], uint32_t (&w)[kAvgChunk
     avg_words<N, Uni>(a, w, tb, offc);
 }
 
+// Uni: at most 64 VGPRs, so 8 wavefronts share a SIMD (the 18 KiB of LDS a
+// 16-worker workgroup takes allow 8 workgroups per CU); left to itself the
+// compiler takes 65, which allows 7.  The general case needs more registers
+// and keeps the default.
 template <bool Pow2K, bool NT, bool Uni>
-__global__ __launch_bounds__(kBlockThreads) void qsgd_average_kernel(QsgdMsgs ms, uint32_t K,
+__global__ __launch_bounds__(kBlockThreads, Uni ? 8 : 1) void qsgd_average_kernel(QsgdMsgs ms, uint32_t K,
                                                                       uint64_t n, uint32_t d,
                                                                       uint32_t s,
                                                                       float kf, uint64_t ntiles,
