@@ -51,7 +51,10 @@ bool valid_threshold(float t) { return isfinite(t) && t > 0.0f; }
 
 bool valid_rate(float eta) { return isfinite(eta) && eta >= 0.0f; }
 
-constexpr size_t kMaxElems = ((size_t)1 << 62);  // keeps every byte count in range
+// Largest element count of a call: with at most 8 bytes per element every
+// byte count stays below 2^63, and with device addresses below 2^48 no
+// range's end address wraps.
+constexpr size_t kMaxElems = GCQ_MAX_ELEMS;
 
 int check_gc2(const float *g, const float *r, size_t n, float t, const uint32_t *out,
               std::vector<Range> *ranges)
@@ -203,7 +206,7 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         return GCQ_ERR_PARAM;
     std::vector<Range> ranges;
     ranges.reserve(3 * (size_t)num_buckets);
-    uint64_t total_tiles = 0;
+    uint64_t total_tiles = 0, total_elems = 0;
     // every bucket spanning the same number of tiles lets the kernel find a
     // tile's bucket by one division
     const gcq_tuning tu = gcq::tuning();
@@ -214,6 +217,9 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         int st = check_gc2(k.g, k.r, k.n, k.t, k.out_words, &ranges);
         if (st != GCQ_OK)
             return st;
+        total_elems += k.n;   // each term <= 2^60, checked as it grows: no wrap
+        if (total_elems > kMaxElems)
+            return GCQ_ERR_PARAM;
         const uint64_t tiles = (k.n + te - 1) / te;
         if (tiles != tpb)
             tpb = 0;

@@ -35,6 +35,8 @@
  *   - Return value: GCQ_OK (0) or a negative GCQ_ERR_* status;
  *     gcq_status_string() names it.
  *   - n == 0 (or W == 0 buckets of work) is a successful no-op.
+ *   - Element counts above 2^60 (GCQ_MAX_ELEMS) are rejected with
+ *     GCQ_ERR_PARAM, so that no byte count or end address can wrap.
  *   - Arithmetic is IEEE float32 with round-to-nearest-even, denormals kept,
  *     no contraction into fused multiply-add where it would change a result.
  */
@@ -52,7 +54,7 @@ enum gcq_status {
     GCQ_OK = 0,
     GCQ_ERR_NULL = -1,      /* a required pointer is NULL while n > 0 */
     GCQ_ERR_THRESHOLD = -2, /* threshold t is not finite or t <= 0 */
-    GCQ_ERR_PARAM = -3,     /* s, d, W or a bucket count out of range */
+    GCQ_ERR_PARAM = -3,     /* n, s, d, W or a bucket count out of range */
     GCQ_ERR_ALIGN = -4,     /* a pointer is not aligned as documented */
     GCQ_ERR_OVERLAP = -5,   /* an output range intersects another operand */
     GCQ_ERR_LAUNCH = -6,    /* the HIP runtime rejected a launch or copy */
@@ -61,6 +63,10 @@ enum gcq_status {
 
 /* Largest W accepted by gc2_dequant_reduce. */
 #define GCQ_MAX_WORKERS 64
+
+/* Largest element count n of any call (and of all buckets of one
+ * gc2_quantize_buckets call together). */
+#define GCQ_MAX_ELEMS ((size_t)1 << 60)
 
 /* ------------------------------------------------------------------ */
 /* 2-bit threshold quantizer with error-feedback residual              */
@@ -119,8 +125,9 @@ typedef struct gc2_bucket {
  *   stream       hipStream_t
  *
  * Errors: as gc2_quantize for any bucket (nothing is launched if one bucket
- * is invalid); GCQ_ERR_OVERLAP also when two buckets' writable ranges (r,
- * out_words) intersect each other or another bucket's g; GCQ_ERR_NOMEM.
+ * is invalid); GCQ_ERR_PARAM when the buckets hold more than GCQ_MAX_ELEMS
+ * elements together; GCQ_ERR_OVERLAP also when two buckets' writable ranges
+ * (r, out_words) intersect each other or another bucket's g; GCQ_ERR_NOMEM.
  */
 int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *stream);
 

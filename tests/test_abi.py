@@ -274,3 +274,46 @@ def test_tuning_roundtrip_and_validation(lib):
     assert gcq.get_tuning()["gc2_blocks_per_cu"] == 7
     gcq.set_tuning(**old)
     assert gcq.get_tuning() == saved
+
+
+def test_element_limit(lib):
+    # n above GCQ_MAX_ELEMS = 2^60 is a parameter error for every call; n at the
+    # limit passes the size check (a NULL operand then reports itself, so
+    # nothing is launched)
+    big, top = (1 << 60) + 1, 1 << 60
+    header = open(HEADER).read()
+    assert "#define GCQ_MAX_ELEMS ((size_t)1 << 60)" in header
+    g, r, o, w = A, A + (1 << 20), A + (2 << 20), A + (3 << 20)
+    q = lambda n_, g_=g: lib.gc2_quantize(vp(g_), vp(r), n_, F(0.5), vp(o), NULL)
+    assert q(big) == E_PARAM and q(top, 0) == E_NULL
+    ws = (ctypes.c_void_p * 2)(A, A + (1 << 20))
+    d = lambda n_, a: lib.gc2_dequant_reduce(ws, 2, n_, F(0.5), vp(a), NULL)
+    assert d(big, w) == E_PARAM and d(top, 0) == E_NULL
+    c = lambda n_, g_=g: lib.cdsgd_update_quantize(vp(g_), vp(r), vp(w), n_, F(0.5), F(0.1), vp(o),
+                                                   NULL)
+    assert c(big) == E_PARAM and c(top, 0) == E_NULL
+    u = lambda n_, g_=g: lib.cdsgd_local_update(vp(g_), vp(w), n_, F(0.1), NULL)
+    assert u(big) == E_PARAM and u(top, 0) == E_NULL
+    for f in (lib.qsgd_quantize, lib.qsgd_quantize_maxnorm):
+        qq = lambda n_, g_=g: f(vp(g_), n_, 512, 7, ctypes.c_uint64(1), vp(r), vp(o), NULL)
+        assert qq(big) == E_PARAM and qq(top, 0) == E_NULL
+    dq = lambda n_, a: lib.qsgd_dequant(vp(r), vp(o), n_, 512, 7, vp(a), NULL)
+    assert dq(big, w) == E_PARAM and dq(top, 0) == E_NULL
+    arr = lambda xs: (ctypes.c_void_p * len(xs))(*[vp(x) for x in xs])
+    av = lambda n_, a: lib.qsgd_dequant_average(arr([r]), arr([o]), 1, n_, 512, 7, vp(a), NULL)
+    assert av(big, w) == E_PARAM and av(top, 0) == E_NULL
+    assert lib.qsgd_elias_max_words(big, 512) == 0
+    e = lambda n_, cap, nm: lib.qsgd_elias_encode(vp(nm), vp(r), n_, 512, vp(o), vp(w), cap, NULL)
+    assert e(big, 100, g) == E_PARAM and e(100, big, g) == E_PARAM and e(top, 100, 0) == E_NULL
+    dd = lambda n_, cnt, nm: lib.qsgd_elias_decode(vp(w), cnt, vp(o), n_, 512, vp(nm), vp(r), NULL)
+    assert dd(big, 10, g) == E_PARAM and dd(100, big, g) == E_PARAM and dd(top, 10, 0) == E_NULL
+    mk = lambda n_, m_: lib.saps_mask(n_, F(100.0), ctypes.c_uint64(5), vp(m_), vp(o), NULL)
+    assert mk(big, r) == E_PARAM and mk(top, 0) == E_NULL
+    for f in (lib.saps_gather, lib.saps_merge):
+        sa = lambda n_, cap, x_: f(vp(x_), n_, vp(r), vp(o), vp(w), cap, NULL)
+        assert sa(big, 10, g) == E_PARAM and sa(100, big, g) == E_PARAM and sa(top, 10, 0) == E_NULL
+    # the fused launch counts every bucket: two of 2^59 + 1 elements are too many together
+    half = (1 << 59) + 1
+    descs = [(A, A + (1 << 20), A + (2 << 20), half, 0.5), (A, A + (3 << 20), A + (4 << 20), half, 0.5)]
+    arrb = (gcq.Gc2Bucket * 2)(*[gcq.Gc2Bucket(*x) for x in descs])
+    assert lib.gc2_quantize_buckets(arrb, 2, NULL) == E_PARAM
