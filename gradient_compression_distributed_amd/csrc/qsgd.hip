@@ -553,10 +553,11 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_lanes_kernel(
 //
 // A workgroup owns a tile of 2048 elements (one nibble word per thread).
 // It first writes an LDS table: for worker l and each bucket the tile
-// touches, the 16 decoded values of the 16 possible nibbles (IEEE division,
-// once per entry).  Then each element and worker costs a nibble extract, a
-// table read and an add; no division per element.  Sums are staged through
-// LDS so every store instruction writes 1 KiB.
+// touches, the 16 decoded values of the 16 possible nibbles (one IEEE
+// division per level, written with both signs).  Then each element and
+// worker costs a nibble extract, a table read and an add; no division per
+// element.  Sums are staged through LDS so every store instruction writes
+// 1 KiB.
 constexpr uint64_t kAvgTileElems = 8u * kBlockThreads;
 constexpr uint32_t kAvgChunk = 16;   // worker words loaded before they are decoded
 // table rows per worker: the buckets a 2048-element tile can touch when
