@@ -317,3 +317,40 @@ def test_element_limit(lib):
     descs = [(A, A + (1 << 20), A + (2 << 20), half, 0.5), (A, A + (3 << 20), A + (4 << 20), half, 0.5)]
     arrb = (gcq.Gc2Bucket * 2)(*[gcq.Gc2Bucket(*x) for x in descs])
     assert lib.gc2_quantize_buckets(arrb, 2, NULL) == E_PARAM
+
+
+# The defaults include/gcq.h documents for each knob (and the environment
+# variable that overrides it).
+DEFAULTS = {"gc2_unroll": 1, "gc2_nt": 7, "gc2_blocks_per_cu": 0, "dq_nt_loads": 1,
+            "dq_nt_stores": 1, "dq_lds_stores": 1, "dq_blocks_per_cu": 0, "dq_fp4_decode": 1,
+            "qsgd_nt": 1, "qsgd_rcp": 1, "qsgd_dequant_nt": 1, "qsgd_blocks_per_cu": 0,
+            "qsgd_dequant_blocks_per_cu": 0, "qsgd_buckets_per_wave": 0, "dq_words_per_thread": 2}
+
+
+def _fresh_tuning(extra_env):
+    import json
+    import subprocess
+    import sys
+
+    env = {k: v for k, v in os.environ.items() if not k.startswith("GCQ_")}
+    env.update(extra_env)
+    code = ("import json, sys; sys.path.insert(0, %r); import gradient_compression_distributed_amd as g; "
+            "print(json.dumps(g.get_tuning()))" % ROOT)
+    p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert p.returncode == 0, p.stderr
+    return json.loads(p.stdout.strip().splitlines()[-1])
+
+
+def test_tuning_defaults_and_environment():
+    assert _fresh_tuning({}) == DEFAULTS
+    header = open(HEADER).read()
+    for knob in DEFAULTS:
+        assert knob in header, knob
+        assert "GCQ_" + knob.upper() in header, knob
+    t = _fresh_tuning({"GCQ_DQ_WORDS_PER_THREAD": "1", "GCQ_GC2_NT": "99",
+                       "GCQ_QSGD_BUCKETS_PER_WAVE": "3", "GCQ_DQ_BLOCKS_PER_CU": "5"})
+    assert t["dq_words_per_thread"] == 1
+    assert t["gc2_nt"] == 15                       # clamped into 0..15
+    assert t["qsgd_buckets_per_wave"] == 0         # invalid: the default
+    assert t["dq_blocks_per_cu"] == 5
