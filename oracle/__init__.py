@@ -29,9 +29,11 @@ passage of the pages it follows:
 * ``omega_length`` / ``qsgd_elias_encode`` / ``qsgd_elias_decode`` -- QSGD
   summary Knowl 2 (norm, then omega-coded distances between non-zero
   coordinates with sign and level), Elias' omega code (1975).
-* ``philox4x32_10`` / ``uniform`` -- the SC'11 Philox-4x32 generator.  The
-  pages name no random source, so the exact uniform stream is
-  "parity unpinned" by the pages; it is pinned only statistically.
+* ``philox4x32_10`` / ``uniform`` -- the SC'11 Philox-4x32 generator,
+  pinned to its published known-answer vectors (``tests/golden/``).  The
+  pages name no random source: which generator, and how (seed, index) map
+  to its key and counter, is a frozen reading; the pages accept any
+  independent uniforms.
 """
 from __future__ import annotations
 

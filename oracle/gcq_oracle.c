@@ -31,10 +31,11 @@
  *         and Adaptive Peer Selection": the shared-seed Bernoulli(1/c)
  *         sparsification mask and the single-peer gossip exchange.
  *   [PH]  Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
- *         1, 2, 3" (SC'11): the Philox-4x32 counter-based generator.  The
- *         pages name no random source; this generator is a frozen choice,
- *         so the exact uniform stream is "parity unpinned" by the pages and
- *         pinned only by statistical tests.
+ *         1, 2, 3" (SC'11): the Philox-4x32 counter-based generator,
+ *         pinned to the authors' published known-answer vectors.  The pages
+ *         name no random source, so the choice of this generator and of the
+ *         (seed, index) -> (key, counter) map is a frozen reading, not
+ *         something the pages fix; any independent uniforms would be correct.
  */
 #include <math.h>
 #include <stddef.h>

@@ -6,6 +6,7 @@ min(n/s^2, sqrt(n)/s) ||v||^2; E||Q||_0 <= s(s + sqrt(n)).  Knowl 2: the
 (norm, sign, level) tuple.  Knowl 8: contiguous buckets of d, one scale per
 bucket, variance bound with d in place of n."""
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -201,6 +202,37 @@ def test_philox_python_twin():
         ctr = [int(x) for x in rs.integers(0, 1 << 32, 4, dtype=np.uint64)]
         key = [int(x) for x in rs.integers(0, 1 << 32, 2, dtype=np.uint64)]
         assert [int(x) for x in oracle.philox4x32_10(ctr, key)] == brute.philox4x32_10(ctr, key)
+
+
+def _philox_kat():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "philox4x32_10_kat.txt")
+    rows = []
+    for ln in open(path):
+        ln = ln.split("#", 1)[0].split()
+        if ln:
+            v = [int(x, 16) for x in ln]
+            assert len(v) == 10
+            rows.append((v[0:4], v[4:6], v[6:10]))
+    assert len(rows) == 3
+    return rows
+
+
+def test_philox_published_known_answers():
+    """The generator against the published Philox-4x32-10 known-answer
+    vectors (Salmon et al., SC'11; the Random123 test file), so that the
+    uniform stream does not rest on a second copy of the same formula."""
+    for ctr, key, want in _philox_kat():
+        assert [int(x) for x in oracle.philox4x32_10(ctr, key)] == want, (ctr, key)
+        assert brute.philox4x32_10(ctr, key) == want, (ctr, key)
+
+
+def test_uniform_from_published_zero_vector():
+    # seed 0, indices 0..3: counter (0, 0, 0, 0) and key (0, 0), the first
+    # published vector; u_i is the top 24 bits of output word i
+    _, _, want = _philox_kat()[0]
+    for i in range(4):
+        assert oracle.uniform(0, i) == (want[i] >> 8) * 2.0 ** -24
 
 
 def test_uniform_depends_on_global_index_only():
