@@ -86,6 +86,8 @@ def _load():
     lib.oracle_qsgd_elias_decode.restype = None
     lib.oracle_saps_keep.argtypes = [u64, u64, f32]
     lib.oracle_saps_keep.restype = ctypes.c_int
+    lib.oracle_saps_keep_range.argtypes = [u64, u64, sz, f32, vp]
+    lib.oracle_saps_keep_range.restype = None
     lib.oracle_saps_gather.argtypes = [vp, sz, f32, u64, vp]
     lib.oracle_saps_gather.restype = sz
     lib.oracle_saps_merge.argtypes = [vp, sz, f32, u64, vp]
@@ -290,11 +292,12 @@ def qsgd_dequant_average(scales: list, nibbles: list, n: int, d: int, s: int) ->
 
 
 def saps_keep(seed: int, n: int, c: float, start: int = 0) -> np.ndarray:
-    """The mask: keep[i] for start <= i < start + n (a bool array; one
-    oracle call each)."""
+    """The mask: keep[i] for start <= i < start + n, as a bool array."""
     lib = _load()
-    return np.array([bool(lib.oracle_saps_keep(seed, i, ctypes.c_float(c)))
-                     for i in range(start, start + n)], dtype=bool)
+    keep = np.empty(n, dtype=np.uint8)
+    lib.oracle_saps_keep_range(ctypes.c_uint64(seed), ctypes.c_uint64(start), n,
+                               ctypes.c_float(c), _ptr(keep))
+    return keep.view(bool)
 
 
 def saps_gather(x: np.ndarray, c: float, seed: int) -> np.ndarray:

@@ -384,6 +384,14 @@ int oracle_saps_keep(uint64_t seed, uint64_t i, float c)
     return u * (double)c < 1.0;
 }
 
+/* keep[j] = oracle_saps_keep(seed, start + j, c) for j < n, one byte each. */
+void oracle_saps_keep_range(uint64_t seed, uint64_t start, size_t n, float c,
+                            unsigned char *keep)
+{
+    for (size_t j = 0; j < n; j++)
+        keep[j] = (unsigned char)oracle_saps_keep(seed, start + j, c);
+}
+
 /* The kept components of x, in index order; returns how many. */
 size_t oracle_saps_gather(const float *x, size_t n, float c, uint64_t seed, float *values)
 {

@@ -7,7 +7,6 @@ import numpy as np
 import pytest
 
 import oracle
-from gradient_compression_distributed_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
@@ -125,39 +124,6 @@ def test_round_trip_on_gpu(gpu):
 def _bits(words, lo, hi):
     w = np.ascontiguousarray(words).astype(">u4").view(np.uint8)
     return np.unpackbits(w)[lo:hi]
-
-
-def test_full_size_sampled(gpu):
-    """2^30 elements, d = 512, s = 7 (the launches the benchmark times):
-    sampled buckets' lengths and bits against the oracle coding them alone,
-    and the decode of sampled buckets."""
-    import torch
-
-    n, d, s = 1 << 30, 512, 7
-    say("elias full size", n)
-    cfg = wl.FUSED_1G
-    g = torch.empty(n, device="cuda")
-    wl.fill_bucketed_normal_(g, cfg, 0)
-    norms, nib = gpu.qsgd_quantize(g, d, s, wl.qsgd_seed(3))
-    del g
-    offs, words = gpu.qsgd_elias_encode(norms, nib, n, d)
-    norms2, nib2 = gpu.qsgd_elias_decode(words, offs, n, d)
-    torch.cuda.synchronize()
-    o = host(offs).astype(np.int64)
-    say("coded bits per element", o[-1] / n)
-    rs = np.random.default_rng(113)
-    nbk = n // d
-    for b in sorted(set([0, nbk - 1] + [int(x) for x in rs.integers(0, nbk, 30)])):
-        nm = host(norms[b:b + 1])
-        nb = host(nib[b * d // 8:(b + 1) * d // 8])
-        oh, wh = oracle.qsgd_elias_encode(nm, nb, d, d)
-        assert o[b + 1] - o[b] == int(oh[-1]), b
-        w0 = o[b] // 32
-        got = _bits(host(words[w0:(o[b + 1] + 31) // 32 + 1]), o[b] - 32 * w0,
-                    o[b + 1] - 32 * w0)
-        assert np.array_equal(got, _bits(wh, 0, int(oh[-1]))), b
-        assert host(norms2[b:b + 1]).view(np.uint32)[0] == nm.view(np.uint32)[0]
-        assert np.array_equal(host(nib2[b * d // 8:(b + 1) * d // 8]), clear_zero_level_signs(nb))
 
 
 def test_decode_into_unaligned_output(gpu):

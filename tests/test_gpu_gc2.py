@@ -347,61 +347,3 @@ def test_bucket_table_cache_over_many_lists(gpu):
     torch.cuda.synchronize()
     for i in range(len(big)):
         assert np.array_equal(host(o_d[i]), oracle.gc2_quantize(gs[i], np.zeros(big[i], np.float32), t))
-
-
-def _code_properties(w32, r_new, v, t):
-    """Per-code facts that hold at any size (checked on the GPU with torch)."""
-    import torch
-
-    n = r_new.numel()
-    k = torch.arange(16, device="cuda", dtype=torch.int32)
-    codes = ((w32.view(-1, 1) >> (30 - 2 * k).view(1, -1)) & 3).view(-1)[:n]
-    assert not bool((codes == 1).any())
-    assert bool((r_new[codes == 3] >= 0).all()) and bool((r_new[codes == 2] <= 0).all())
-    z = codes == 0
-    assert torch.equal(r_new[z].view(torch.int32), v[z].view(torch.int32))
-    assert bool((r_new[z].abs() < t).all())
-
-
-def test_1g_full_size_fused(gpu):
-    """1G elements, 128 fusion buckets, the fused launch the benchmark times:
-    sampled buckets bit-exact against the oracle over two steps (the oracle
-    chains its own residual), fused == per-bucket launches on every bucket,
-    and the per-code facts on every element."""
-    import torch
-
-    cfg = wl.FUSED_1G
-    say("gc2 2^30 fused full size", cfg.n)
-    nb = cfg.n // cfg.block
-    g = torch.empty(cfg.n, device="cuda")
-    r = torch.zeros(cfg.n, device="cuda")
-    r2 = torch.zeros(cfg.n, device="cuda")
-    words = torch.empty(cfg.n // 16, dtype=torch.int32, device="cuda")
-    words2 = torch.empty_like(words)
-    wpb = cfg.block // 16
-    bk = [(g[b * cfg.block:(b + 1) * cfg.block], r[b * cfg.block:(b + 1) * cfg.block],
-           words[b * wpb:(b + 1) * wpb], cfg.t) for b in range(nb)]
-    sample = [0, 37, 90, nb - 1]
-    r_h = {b: np.zeros(cfg.block, np.float32) for b in sample}
-    for step in range(2):
-        wl.fill_bucketed_normal_(g, cfg, step)
-        g_h = {b: g[b * cfg.block:(b + 1) * cfg.block].cpu().numpy() for b in sample}
-        r_prev = r.clone()
-        gpu.gc2_quantize_buckets(bk)
-        for b in range(nb):
-            sl = slice(b * cfg.block, (b + 1) * cfg.block)
-            gpu.gc2_quantize(g[sl], r2[sl], cfg.t, out=words2[b * wpb:(b + 1) * wpb])
-        torch.cuda.synchronize()
-        say("step", step, "launched")
-        assert torch.equal(words, words2)
-        assert torch.equal(r.view(torch.int32), r2.view(torch.int32))
-        for b in sample:
-            w_h = oracle.gc2_quantize(g_h[b], r_h[b], cfg.t)
-            assert np.array_equal(host(words[b * wpb:(b + 1) * wpb]), w_h), (step, b)
-            assert np.array_equal(bits(host(r[b * cfg.block:(b + 1) * cfg.block])),
-                                  bits(r_h[b])), (step, b)
-        for b in range(0, nb, 8):
-            sl = slice(b * cfg.block, (b + 1) * cfg.block)
-            v = g[sl] + r_prev[sl]
-            _code_properties(words[b * wpb:(b + 1) * wpb], r[sl], v, cfg.t)
-        del r_prev

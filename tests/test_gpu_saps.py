@@ -9,7 +9,6 @@ import numpy as np
 import pytest
 
 import oracle
-from gradient_compression_distributed_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
@@ -141,51 +140,6 @@ def test_two_peers_agree_after_exchange(gpu):
     assert np.array_equal(ah[kept], bh[kept])
     oracle.saps_merge(a, c, seed, host(vb))
     assert np.array_equal(ah, a)
-
-
-def test_full_size_sampled(gpu):
-    """2^30 elements at c = 100 (the launches the benchmark times): the mask
-    and offsets of sampled tiles, the total, and gathered / merged values
-    there, against the oracle."""
-    import torch
-
-    n, c, seed = 1 << 30, 100.0, wl.qsgd_seed(5)
-    say("saps full size", n)
-    x = torch.empty(n, device="cuda")
-    wl.fill_normal_(x, 8, 1, 1.0)
-    mask, offs = gpu.saps_mask(n, c, seed)
-    total = gpu.saps_count(offs)
-    vals = gpu.saps_gather(x, mask, offs)
-    peer = torch.empty(total, device="cuda")
-    wl.fill_normal_(peer, 8, 2, 1.0)
-    x2 = x.clone()
-    gpu.saps_merge(x2, mask, offs, peer)
-    torch.cuda.synchronize()
-    say("launched, kept", total)
-    mu, sd = n / c, np.sqrt(n / c)
-    assert abs(total - mu) < 6 * sd
-    lib = oracle._load()
-    import ctypes
-    rs = np.random.default_rng(94)
-    o = host(offs)
-    tiles = sorted(set([0, n // TILE - 1] + [int(t) for t in rs.integers(0, n // TILE, 12)]))
-    for t in tiles:
-        e0 = t * TILE
-        kept = np.array([i for i in range(e0, e0 + TILE)
-                         if lib.oracle_saps_keep(seed, i, ctypes.c_float(c))], dtype=np.int64)
-        words = host(mask[e0 // 32:(e0 + TILE) // 32])
-        want = np.zeros(TILE // 32, np.uint64)
-        np.add.at(want, (kept - e0) // 32,
-                  np.left_shift(np.uint64(1), ((kept - e0) % 32).astype(np.uint64)))
-        assert np.array_equal(words, want.astype(np.uint32)), t
-        r0, r1 = int(o[t]), int(o[t + 1])
-        assert r1 - r0 == kept.size, t
-        xs = host(x[e0:e0 + TILE])
-        assert np.array_equal(host(vals[r0:r1]), xs[kept - e0]), t
-        ps = host(peer[r0:r1])
-        want_x = xs.copy()
-        want_x[kept - e0] = (xs[kept - e0] + ps) * np.float32(0.5)
-        assert np.array_equal(host(x2[e0:e0 + TILE]), want_x), t
 
 
 def test_offsets_across_scan_chunks(gpu):

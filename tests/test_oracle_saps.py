@@ -41,6 +41,21 @@ def test_mask_matches_independent_generator():
             assert np.array_equal(_kept_indices(n, c, seed), want), (seed, c)
 
 
+def test_keep_range_at_any_start():
+    # the per-range mask the whole-size GPU tests use: element start + j is
+    # kept exactly when the independent generator's draw for that global
+    # index says so, whatever the start (a multiple of 4 or not)
+    seed, c, n = 0xDEADBEEF12345678, 3.5, 9_001
+    for start in (0, 1, 12_345, (1 << 33) + 3):
+        q = np.arange(start >> 2, ((start + n + 3) >> 2) + 1, dtype=np.uint64)
+        words = brute.philox4x32_10_np(q & np.uint64(0xFFFFFFFF), q >> np.uint64(32), 0, 0,
+                                       seed & 0xFFFFFFFF, seed >> 32)
+        w = np.stack(words, axis=1).reshape(-1)
+        U = (w >> np.uint64(8)).astype(np.float64)[start - 4 * (start >> 2):][:n]
+        want = U * float(F(c)) < 2.0 ** 24
+        assert np.array_equal(oracle.saps_keep(seed, n, c, start=start), want), start
+
+
 def test_exact_threshold_at_powers_of_two():
     # c = 2^k: kept exactly when the 24-bit draw U < 2^(24-k); u c == 1 is dropped
     n = 40_000
