@@ -13,12 +13,17 @@ buckets of 8,388,608, t = 1e-3):
 Inputs are generated on the device before the timed region (seeded torch
 RNG); a new gradient per step, cycling through up to four buffers.
 
-Prints ONE JSON line.  `value` is whole-step throughput in elements of the
-batch per second; `ops` breaks each operation down (elements/s, GB/s of
-algorithmic traffic, fraction of the 8 TB/s HBM peak); `roofline` is the
-dominant kernel (the fused 2-bit quantizer) timed with HIP events on the
-stream it is launched on; `cpu_baseline` is the CPU oracle on a bounded
-sample of the same workload, single-threaded on this host.
+Prints ONE JSON line.  `value` is the fused 2-bit quantizer's throughput
+in elements per second (the metric); the whole step's rate is
+`step_elements_per_s`.  `ops` breaks each operation down (elements/s, GB/s
+of algorithmic traffic, fraction of the 8 TB/s HBM peak and of the
+streaming probe with the same access pattern); `roofline` is the dominant
+kernel (the fused 2-bit quantizer) timed with HIP events on the stream it
+is launched on; `ceiling` holds the measured practical ceilings (the
+runtime's 4 GiB device copy and the library's streaming probes);
+`configs` times the four smaller workloads (median and best of at least
+10 repetitions); `cpu_baseline` is the CPU oracle on a bounded sample of
+the same workload, single-threaded on this host.
 """
 from __future__ import annotations
 
@@ -53,19 +58,25 @@ KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gc2_quantize.hip", "gcq_device.h
                                                "gcq_internal.h")]
 
 
+PHASE = 32768   # offsets of the views are placed modulo this many bytes
+
+
 def arena(layout, dev):
-    """Views of one device allocation, one per (numel, dtype) in `layout`,
-    each starting on a 4 KiB boundary."""
+    """Views of one device allocation, one per (numel, dtype, phase) in
+    `layout`: each starts on a 4 KiB boundary whose offset modulo 32 KiB is
+    `phase` (two buffers streamed at the same index, like a gradient and its
+    residual, run slower when their addresses agree modulo 32 KiB)."""
     import torch
 
     offs, total = [], 0
-    for numel, dt in layout:
+    for numel, dt, phase in layout:
+        total = (total + 4095) // 4096 * 4096
+        total += (phase - total) % PHASE
         offs.append(total)
-        nbytes = numel * torch.tensor([], dtype=dt).element_size()
-        total += (nbytes + 4095) // 4096 * 4096
+        total += numel * torch.tensor([], dtype=dt).element_size()
     buf = torch.empty(total, dtype=torch.uint8, device=dev)
     return [buf[o:o + numel * torch.tensor([], dtype=dt).element_size()].view(dt)
-            for o, (numel, dt) in zip(offs, layout)]
+            for o, (numel, dt, _) in zip(offs, layout)]
 
 
 def kernel_source_sha() -> str:
@@ -102,8 +113,12 @@ def parse():
                    help="skip the 128-launch comparison of the fused quantizer")
     p.add_argument("--no-next", action="store_true",
                    help="skip timing CD-SGD's fused local update + quantize")
-    p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a 4 GiB device copy (reference kernel for counters)")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the device copy and the streaming probes")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip timing the four smaller workloads")
+    p.add_argument("--config-reps", type=int, default=10,
+                   help="timed repetitions per smaller workload (at least 10)")
     return p.parse_args()
 
 
@@ -131,15 +146,17 @@ def main():
 
     # ---------------------------------------------------------- setup (untimed)
     # Every buffer of the step is a view into one device allocation, as a
-    # flat data-parallel gradient buffer would be.  (With one allocation per
-    # 4 GiB buffer, one of the four gradient buffers ran the quantizer about
-    # 6% slower than the others, on every box tried.)
+    # flat data-parallel gradient buffer would be.  Where each starts modulo
+    # 32 KiB was measured in this layout on two boxes, with the same result:
+    # the residual at a multiple of 8 KiB from the gradients (here 0; odd
+    # multiples of 4 KiB ran the quantizer 1-3% slower), and the sums 16 KiB
+    # off the workers' packed buffers (the reduce 1-2% faster than at 0).
     ngrad = min(K + Wm, 4)
     nw = n // 16
-    layout = ([(n, torch.float32)] * ngrad + [(n, torch.float32)] +
-              [(nw, torch.int32)] * W_WORKERS + [(n, torch.float32)] +
-              [(gcq.qsgd_num_buckets(n, QSGD_D), torch.float32),
-               (gcq.qsgd_nibble_words(n), torch.int32), (n, torch.float32)])
+    layout = ([(n, torch.float32, 0)] * ngrad + [(n, torch.float32, 0)] +
+              [(nw, torch.int32, 0)] * W_WORKERS + [(n, torch.float32, 16384)] +
+              [(gcq.qsgd_num_buckets(n, QSGD_D), torch.float32, 0),
+               (gcq.qsgd_nibble_words(n), torch.int32, 0), (n, torch.float32, 0)])
     views = arena(layout, dev)
     grads = views[:ngrad]
     r = views[ngrad]
@@ -313,18 +330,21 @@ def main():
                                                    "coded_bits_per_element": coded_bits / n}
         del eoffs, ewords, nib2, norms2
 
-    copy_gbps = None
-    if args.copy_calibration:
-        src = grads[0]
-        dst = acc
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        dst.copy_(src)
-        e0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * 4 * n / (e0.elapsed_time(e1) / 5 / 1e3) / 1e9
+    # practical ceilings, after everything else (they overwrite the step's
+    # buffers): the runtime's 4 GiB device copy, and the library's probes
+    # with the exact access patterns of the quantizer and the reduce on the
+    # same buffers (no arithmetic)
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = measure_ceilings(gcq, np, torch, n, grads, r, words, acc, qout)
+        ops["gc2_quantize_buckets"]["frac_of_probe"] = round(
+            ops["gc2_quantize_buckets"]["GBps"] / ceiling["probe_quantize_GBps"], 4)
+        ops["gc2_dequant_reduce"]["frac_of_probe"] = round(
+            ops["gc2_dequant_reduce"]["GBps"] / ceiling["probe_reduce_GBps"], 4)
+
+    configs = None
+    if not args.no_configs:
+        configs = time_configs(args, gcq, wl, np, torch, dev)
 
     q_ms = op_ms["gc2_quantize_buckets"]
     achieved = BYTES["gc2_quantize_buckets"] * n / (q_ms / 1e3) / 1e9
@@ -339,7 +359,8 @@ def main():
         cpu = cpu_baseline(args, cfg, grads[0], words, np, torch, wl)
 
     line = {
-        "metric": METRIC, "value": n / (ms_per_step / 1e3), "unit": "elements/s",
+        "metric": METRIC, "value": ops["gc2_quantize_buckets"]["elements_per_s"],
+        "unit": "elements/s",
         "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded device RNG; per-bucket N(0, sigma_b^2), "
@@ -352,11 +373,113 @@ def main():
         "cpu_baseline": cpu,
         "ops": ops,
         "next_ops": next_ops,
-        "gc2_quantize_elements_per_s": ops["gc2_quantize_buckets"]["elements_per_s"],
-        "device_copy_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+        "step_elements_per_s": n / (ms_per_step / 1e3),
+        "ceiling": ceiling,
+        "configs": configs,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_ceilings(gcq, np, torch, n, grads, r, words, acc, out, reps=10):
+    """GB/s of the runtime's 4 GiB device copy and of the library's probes
+    (median of `reps` launches, HIP events on the current stream)."""
+    def med(fn, bpe):
+        ts = _event_times(torch, lambda i: fn(), 2, reps)
+        return round(bpe * n / (float(np.median(ts)) / 1e3) / 1e9, 1)
+
+    return {
+        "device_copy_GBps": med(lambda: out.copy_(grads[0]), 8.0),
+        "probe_copy_GBps": med(lambda: gcq.probe_stream(grads[0], out), 8.0),
+        "probe_quantize_GBps": med(lambda: gcq.probe_stream(grads[0], r, b=r, words=words[0]),
+                                   BYTES["gc2_quantize_buckets"]),
+        "probe_reduce_GBps": med(lambda: gcq.probe_reduce(words, n, acc),
+                                 BYTES["gc2_dequant_reduce"]),
+        "note": "device_copy: torch copy_ of 4 GiB (the runtime's copy kernel); probe_copy: "
+                "the library's float4 copy in the quantizer's geometry; probe_quantize: the "
+                "quantizer's streams (g read, r read and written in place, packed words "
+                "written) with no arithmetic; probe_reduce: the reduce's own kernel with the "
+                "decode replaced by an XOR; all at 2^30 elements on the step's buffers",
+    }
+
+
+def _event_times(torch, fn, warm, reps):
+    """Per-call HIP-event times (ms) of `fn(i)` on the current stream for
+    i = warm .. warm + reps - 1, after `warm` untimed calls."""
+    for i in range(warm):
+        fn(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record()
+        fn(warm + k)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _summary(np, ts, n, bpe):
+    med, best = float(np.median(ts)), float(min(ts))
+    gbps = bpe * n / (med / 1e3) / 1e9
+    return {"ms_median": round(med, 4), "ms_best": round(best, 4), "reps": len(ts),
+            "elements_per_s": n / (med / 1e3), "GBps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_element": round(bpe, 4)}
+
+
+def time_configs(args, gcq, wl, np, torch, dev):
+    """The four smaller workloads, each op timed per call with HIP events
+    (median and best of `reps`; inputs resident on the device; multi-step
+    workloads cycle through their steps, the residual carried).  Their
+    working sets fit partly in the 256 MB last-level cache, so they are
+    reported, not used for the roofline."""
+    reps = max(10, args.config_reps)
+    out = {}
+    # 2-bit quantize + residual, 65,541 elements, 3 steps of fresh g
+    c1 = wl.GC2_RAGGED_65K
+    g1 = [torch.from_numpy(wl.gradient(c1, s)).to(dev) for s in range(c1.steps)]
+    r1 = torch.zeros(c1.n, device=dev)
+    o1 = torch.empty(gcq.gc2_packed_words(c1.n), dtype=torch.int32, device=dev)
+    ts = _event_times(torch, lambda i: gcq.gc2_quantize(g1[i % c1.steps], r1, c1.t, out=o1), 3, reps)
+    out["gc2_ragged_65k"] = {"op": "gc2_quantize", "n": c1.n, "t": c1.t,
+                             **_summary(np, ts, c1.n, BYTES["gc2_quantize_buckets"])}
+    del g1, r1, o1
+    # 2-bit quantize + residual, ResNet-50-sized, 10 steps
+    c2 = wl.GC2_RESNET50
+    g2 = [torch.from_numpy(wl.gradient(c2, s)).to(dev) for s in range(c2.steps)]
+    r2 = torch.zeros(c2.n, device=dev)
+    o2 = torch.empty(gcq.gc2_packed_words(c2.n), dtype=torch.int32, device=dev)
+    ts = _event_times(torch, lambda i: gcq.gc2_quantize(g2[i % c2.steps], r2, c2.t, out=o2), 3, reps)
+    out["gc2_resnet50"] = {"op": "gc2_quantize", "n": c2.n, "t": c2.t,
+                           **_summary(np, ts, c2.n, BYTES["gc2_quantize_buckets"])}
+    del g2, r2, o2
+    # dequantize-and-reduce, 16 workers, ResNet-50-sized
+    c3 = wl.REDUCE_W16_RESNET50
+    nw3 = gcq.gc2_packed_words(c3.n)
+    w3 = [torch.empty(nw3, dtype=torch.int32, device=dev) for _ in range(c3.workers)]
+    for k, w in enumerate(w3):
+        wl.fill_iid_field_words_(w, c3.stream, k)
+    a3 = torch.empty(c3.n, device=dev)
+    ts = _event_times(torch, lambda i: gcq.gc2_dequant_reduce(w3, c3.n, c3.t, acc=a3), 3, reps)
+    out["reduce_w16_resnet50"] = {"op": "gc2_dequant_reduce", "n": c3.n, "W": c3.workers,
+                                  "t": c3.t, **_summary(np, ts, c3.n, c3.workers * 0.25 + 4.0)}
+    del w3, a3
+    # QSGD quantize and dequant, AlexNet-sized, d = 512, s = 7
+    c4 = wl.QSGD_ALEXNET
+    g4 = torch.from_numpy(wl.gradient(c4, 0)).to(dev)
+    nm4 = torch.empty(gcq.qsgd_num_buckets(c4.n, c4.d), device=dev)
+    nb4 = torch.empty(gcq.qsgd_nibble_words(c4.n), dtype=torch.int32, device=dev)
+    q4 = torch.empty(c4.n, device=dev)
+    ts_q = _event_times(torch, lambda i: gcq.qsgd_quantize(g4, c4.d, c4.s, wl.qsgd_seed(i),
+                                                           norms=nm4, nibbles=nb4), 3, reps)
+    ts_d = _event_times(torch, lambda i: gcq.qsgd_dequant(nm4, nb4, c4.n, c4.d, c4.s, out=q4),
+                        3, reps)
+    bq = 4.0 + 0.5 + 4.0 / c4.d
+    out["qsgd_alexnet"] = {"n": c4.n, "d": c4.d, "s": c4.s,
+                           "qsgd_quantize": _summary(np, ts_q, c4.n, bq),
+                           "qsgd_dequant": _summary(np, ts_d, c4.n, bq)}
+    del g4, nm4, nb4, q4
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
@@ -392,9 +515,11 @@ def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
         total += t4 - t0
         elems += blk
         b += 1
-    # the widened rows, timed the same way on a 2^21-element sample of the
-    # same gradient (inputs that are another row's output are made untimed)
-    m = 1 << 21
+    # the widened rows, timed the same way on one whole bucket of the same
+    # gradient, 2^23 elements (32 MiB per float array, so the streaming rows
+    # do not run from the host's caches; inputs that are another row's output
+    # are made untimed)
+    m = cfg.block
     gs = g_dev[:m].cpu().numpy()
     cds = wl.CDSGD_1G
     rs = np.random.default_rng(7)
@@ -440,9 +565,9 @@ def cpu_baseline(args, cfg, g_dev, words, np, torch, wl):
             "seconds": round(total, 3),
             "ops_elements_per_s": {op: elems / s for op, s in per_op.items()},
             "next_ops_elements_per_s": nxt,
-            "next_ops_sample": f"{m} elements of the same gradient, each widened operation once "
-                               f"(K = {W_WORKERS} messages for the average, c = {SAPS_C} for SAPS); "
-                               "arrays of this size stay in the host's caches",
+            "next_ops_sample": f"{m} elements (one bucket) of the same gradient, each widened "
+                               f"operation once (K = {W_WORKERS} messages for the average, "
+                               f"c = {SAPS_C} for SAPS); 32 MiB per float array",
             "host_cpus": os.cpu_count(), "cpu_model": model}
 
 

@@ -23,6 +23,7 @@ __all__ = [
     "qsgd_quantize_maxnorm", "qsgd_dequant_average",
     "saps_mask", "saps_gather", "saps_merge", "saps_mask_words", "saps_num_tiles",
     "qsgd_elias_encode", "qsgd_elias_decode", "qsgd_elias_max_words",
+    "probe_stream", "probe_reduce",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +46,8 @@ class Tuning(ctypes.Structure):
         "gc2_unroll", "gc2_nt", "gc2_blocks_per_cu", "dq_nt_loads", "dq_nt_stores",
         "dq_lds_stores", "dq_blocks_per_cu", "dq_fp4_decode", "qsgd_nt", "qsgd_rcp",
         "qsgd_dequant_nt", "qsgd_blocks_per_cu", "qsgd_dequant_blocks_per_cu",
-        "qsgd_buckets_per_wave", "dq_words_per_thread")]
+        "qsgd_buckets_per_wave", "dq_words_per_thread", "dq_resident_per_cu",
+        "gc2_resident_per_cu")]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -78,6 +80,10 @@ def load():
     lib.gc2_quantize_buckets.restype = i32
     lib.gc2_dequant_reduce.argtypes = [ctypes.POINTER(vp), u32, sz, f32, vp, vp]
     lib.gc2_dequant_reduce.restype = i32
+    lib.gcq_probe_reduce.argtypes = [ctypes.POINTER(vp), u32, sz, vp, vp]
+    lib.gcq_probe_reduce.restype = i32
+    lib.gcq_probe_stream.argtypes = [vp, vp, vp, vp, sz, vp]
+    lib.gcq_probe_stream.restype = i32
     lib.qsgd_quantize.argtypes = [vp, sz, u32, u32, u64, vp, vp, vp]
     lib.qsgd_quantize.restype = i32
     lib.qsgd_dequant.argtypes = [vp, vp, sz, u32, u32, vp, vp]
@@ -292,6 +298,41 @@ def gc2_dequant_reduce(words, n: int, t: float, acc=None):
     ptrs = (ctypes.c_void_p * max(W, 1))(*[w.data_ptr() for w in words])
     _check(lib.gc2_dequant_reduce(ptrs, W, n, ctypes.c_float(t), _ptr(acc),
                                   _stream(acc.device)), "gc2_dequant_reduce")
+    return acc
+
+
+def probe_stream(a, c, b=None, words=None):
+    """Measurement probe with the 2-bit quantizer's access pattern and no
+    arithmetic: c = a ^ b (bitwise; c = a without b), plus a packed-word
+    stream when ``words`` is given.  n = a.numel() must be a multiple of 1024."""
+    import torch
+
+    lib = load()
+    _dev(a, torch.float32, "a")
+    n = a.numel()
+    _dev(c, torch.float32, "c", n)
+    if b is not None:
+        _dev(b, torch.float32, "b", n)
+    if words is not None:
+        _dev(words, torch.int32, "words", n // 16)
+    _check(lib.gcq_probe_stream(_ptr(a), _ptr(b) if b is not None else None, _ptr(c),
+                                _ptr(words) if words is not None else None, n,
+                                _stream(a.device)), "gcq_probe_stream")
+
+
+def probe_reduce(words, n: int, acc):
+    """Measurement probe: gc2_dequant_reduce's kernel with the decode replaced
+    by an XOR (acc[16 i] = XOR of the workers' word i, other sums +0)."""
+    import torch
+
+    lib = load()
+    W = len(words)
+    nw = gc2_packed_words(n)
+    for i, w in enumerate(words):
+        _dev(w, torch.int32, f"words[{i}]", nw)
+    _dev(acc, torch.float32, "acc", n)
+    ptrs = (ctypes.c_void_p * max(W, 1))(*[w.data_ptr() for w in words])
+    _check(lib.gcq_probe_reduce(ptrs, W, n, _ptr(acc), _stream(acc.device)), "gcq_probe_reduce")
     return acc
 
 

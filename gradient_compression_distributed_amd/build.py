@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgcq.so")
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("gc2_quantize.hip", "dequant_reduce.hip", "qsgd.hip", "saps.hip", "elias.hip", "gcq_runtime.hip",
+           ("gc2_quantize.hip", "dequant_reduce.hip", "qsgd.hip", "saps.hip", "elias.hip", "probe.hip", "gcq_runtime.hip",
             "gcq_api.hip")]
 ARCH = os.environ.get("GCQ_OFFLOAD_ARCH", "gfx950")
 

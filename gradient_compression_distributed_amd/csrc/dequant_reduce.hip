@@ -14,6 +14,9 @@ namespace gcq {
 
 namespace {
 
+using dev::kBufferRsrcWord3;
+using dev::kCpolNt;
+using dev::kCpolSc1;
 using dev::ld;
 using dev::st;
 using dev::v4f;
@@ -44,7 +47,10 @@ __device__ __forceinline__ uint32_t signed_pairs(uint32_t w)
 //   tq = t/64.
 // kDecodePlain: f from a sign-extending shift, tq = t (any t, including
 //   t < 2^-120, where t/2 or t/64 would not be exact).
-enum { kDecodeFp4 = 0, kDecodeSdwa = 1, kDecodePlain = 2 };
+// kProbe (measurement only): no decode at all, the word is XORed into the
+//   first sum, so the kernel keeps its loads, staging and stores and does
+//   no arithmetic (gcq_probe_reduce).
+enum { kDecodeFp4 = 0, kDecodeSdwa = 1, kDecodePlain = 2, kProbe = 3 };
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
@@ -64,6 +70,10 @@ __device__ __forceinline__ void fp4_byte(float (&a)[16], uint32_t me, uint32_t m
 template <int Mode>
 __device__ __forceinline__ void accumulate(float (&a)[16], uint32_t w, float tq)
 {
+    if constexpr (Mode == kProbe) {
+        a[0] = __uint_as_float(__float_as_uint(a[0]) ^ w);
+        return;
+    }
     const uint32_t pairs = signed_pairs(w);
     if constexpr (Mode == kDecodeFp4) {
         const uint32_t me = pairs & 0xCCCCCCCCu;
@@ -89,6 +99,23 @@ __device__ __forceinline__ void accumulate(float (&a)[16], uint32_t w, float tq)
             const float v = (float)((int32_t)(pairs << (2 * k)) >> 30);
             a[k] = __builtin_fmaf(tq, v, a[k]);
         }
+    }
+}
+
+// Store of 16 bytes of a full tile's sums, `off` bytes into a wavefront's
+// run of `bytes` consecutive bytes at `base`.  NTS: a buffer store with the
+// nt and sc1 cache-policy bits, which ran the 2^30-element, 16-worker reduce
+// about 2% faster than nt alone; otherwise a plain store.
+template <bool NTS>
+__device__ __forceinline__ void st_run(GCQ_GLOBAL float *base, uint32_t bytes, uint32_t off,
+                                       v4f x)
+{
+    if constexpr (NTS) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, kBufferRsrcWord3);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rs, (int)off, 0, kCpolNt | kCpolSc1);
+    } else {
+        *(GCQ_GLOBAL v4f *)((GCQ_GLOBAL char *)base + off) = x;
     }
 }
 
@@ -160,7 +187,7 @@ __global__ __launch_bounds__(kBlockThreads) void dq_reduce_kernel(DqWorkers ws, 
             for (int q = 0; q < 4; ++q) {
                 // element 256q + 4L of the wave tile: row 16q + L/4, column 4(L%4)
                 const v4f x = wstage[(16 * q + (lane >> 2)) * (kLdsRow / 4) + (lane & 3)];
-                st<NTS>((GCQ_GLOBAL v4f *)(out + e0) + 64 * q + lane, x);
+                st_run<NTS>(out + e0, kWave * 16 * 4, (64 * q + lane) * 16, x);
             }
             __syncthreads();
         } else if (valid) {
@@ -262,7 +289,7 @@ __global__ __launch_bounds__(kBlockThreads) void dq_reduce2_kernel(DqWorkers ws,
             for (int q = 0; q < 8; ++q) {
                 // element 256q + 4L of the wave tile: row 8q + L/8, column 4(L%8)
                 const v4f x = wstage[(8 * q + (lane >> 3)) * (kRow2 / 4) + (lane & 7)];
-                st<NTS>((GCQ_GLOBAL v4f *)(out + e0) + 64 * q + lane, x);
+                st_run<NTS>(out + e0, kWave * 32 * 4, (64 * q + lane) * 16, x);
             }
             __syncthreads();
         } else {
@@ -278,11 +305,11 @@ __global__ __launch_bounds__(kBlockThreads) void dq_reduce2_kernel(DqWorkers ws,
 }
 
 template <int Mode, bool NTL, bool NTS, bool Lds>
-void launch_one(uint32_t grid, hipStream_t stream, const DqWorkers &ws, uint32_t W,
+void launch_one(uint32_t grid, uint32_t pad, hipStream_t stream, const DqWorkers &ws, uint32_t W,
                 uint32_t nwords, uint64_t n, float tq, float *acc)
 {
     dq_reduce_kernel<Mode, NTL, NTS, Lds>
-        <<<grid, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+        <<<grid, kBlockThreads, pad, stream>>>(ws, W, nwords, n, tq, acc);
 }
 
 template <int Mode>
@@ -292,27 +319,30 @@ void dispatch(const gcq_tuning &tu, uint32_t grid, hipStream_t stream, const DqW
     if (two) {
         const uint32_t grid2 = grid_for((nwords + 2u * kBlockThreads - 1) / (2u * kBlockThreads),
                                         tu.dq_blocks_per_cu);
+        const uint32_t pad = resident_lds_pad(kBlockWaves * kWave * kRow2 * 4, tu.dq_resident_per_cu);
         const int k2 = tu.dq_nt_loads * 2 + tu.dq_nt_stores;
         if (k2 == 3)
-            dq_reduce2_kernel<Mode, true, true><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+            dq_reduce2_kernel<Mode, true, true><<<grid2, kBlockThreads, pad, stream>>>(ws, W, nwords, n, tq, acc);
         else if (k2 == 2)
-            dq_reduce2_kernel<Mode, true, false><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+            dq_reduce2_kernel<Mode, true, false><<<grid2, kBlockThreads, pad, stream>>>(ws, W, nwords, n, tq, acc);
         else if (k2 == 1)
-            dq_reduce2_kernel<Mode, false, true><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+            dq_reduce2_kernel<Mode, false, true><<<grid2, kBlockThreads, pad, stream>>>(ws, W, nwords, n, tq, acc);
         else
-            dq_reduce2_kernel<Mode, false, false><<<grid2, kBlockThreads, 0, stream>>>(ws, W, nwords, n, tq, acc);
+            dq_reduce2_kernel<Mode, false, false><<<grid2, kBlockThreads, pad, stream>>>(ws, W, nwords, n, tq, acc);
         return;
     }
+    const uint32_t pad = resident_lds_pad(tu.dq_lds_stores ? kBlockWaves * kWave * kLdsRow * 4 : 16,
+                                 tu.dq_resident_per_cu);
     const int key = tu.dq_nt_loads * 4 + tu.dq_nt_stores * 2 + tu.dq_lds_stores;
     switch (key) {
-    case 0: launch_one<Mode, false, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 1: launch_one<Mode, false, false, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 2: launch_one<Mode, false, true, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 3: launch_one<Mode, false, true, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 4: launch_one<Mode, true, false, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 5: launch_one<Mode, true, false, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    case 6: launch_one<Mode, true, true, false>(grid, stream, ws, W, nwords, n, tq, acc); break;
-    default: launch_one<Mode, true, true, true>(grid, stream, ws, W, nwords, n, tq, acc); break;
+    case 0: launch_one<Mode, false, false, false>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    case 1: launch_one<Mode, false, false, true>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    case 2: launch_one<Mode, false, true, false>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    case 3: launch_one<Mode, false, true, true>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    case 4: launch_one<Mode, true, false, false>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    case 5: launch_one<Mode, true, false, true>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    case 6: launch_one<Mode, true, true, false>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
+    default: launch_one<Mode, true, true, true>(grid, pad, stream, ws, W, nwords, n, tq, acc); break;
     }
 }
 
@@ -322,7 +352,7 @@ constexpr uint64_t kMaxWordsPerLaunch = (uint64_t)1 << 30;
 }  // namespace
 
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t, float *acc,
-                                 hipStream_t stream)
+                                 hipStream_t stream, bool probe)
 {
     const uint64_t nwords = (n + 15) >> 4;
     if (!nwords)
@@ -330,7 +360,9 @@ hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, flo
     const gcq_tuning tu = tuning();
     // t/2 and t/64 are exact (power-of-two scalings that stay normal) for
     // t >= 2^-120; smaller thresholds use the plain decode.
-    const int mode = t < 0x1p-120f ? kDecodePlain : (tu.dq_fp4_decode ? kDecodeFp4 : kDecodeSdwa);
+    const int mode = probe ? kProbe
+                           : t < 0x1p-120f ? kDecodePlain
+                                           : (tu.dq_fp4_decode ? kDecodeFp4 : kDecodeSdwa);
     const float tq = mode == kDecodeFp4 ? t * 0.5f : (mode == kDecodeSdwa ? t * 0x1p-6f : t);
     for (uint64_t w0 = 0; w0 < nwords; w0 += kMaxWordsPerLaunch) {
         const uint64_t cw = nwords - w0 < kMaxWordsPerLaunch ? nwords - w0 : kMaxWordsPerLaunch;
@@ -344,7 +376,9 @@ hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, flo
         bool two = tu.dq_words_per_thread == 2;
         for (uint32_t k = 0; k < W; ++k)
             two = two && ((uintptr_t)ws.w[k] & 7u) == 0;
-        if (mode == kDecodeFp4)
+        if (mode == kProbe)
+            dispatch<kProbe>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16, two);
+        else if (mode == kDecodeFp4)
             dispatch<kDecodeFp4>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16, two);
         else if (mode == kDecodeSdwa)
             dispatch<kDecodeSdwa>(tu, grid, stream, ws, W, (uint32_t)cw, cn, tq, acc + w0 * 16, two);

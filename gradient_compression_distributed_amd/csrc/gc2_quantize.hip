@@ -221,13 +221,13 @@ __global__ __launch_bounds__(kBlockThreads) void gc2_quantize_kernel(
 }
 
 template <int U, bool Table>
-void launch_nt(int nt, uint32_t grid, const Gc2Desc &one, const Gc2Desc *table, uint32_t nb,
-               uint64_t total_tiles, uint32_t tpb, hipStream_t stream)
+void launch_nt(int nt, uint32_t grid, uint32_t pad, const Gc2Desc &one, const Gc2Desc *table,
+               uint32_t nb, uint64_t total_tiles, uint32_t tpb, hipStream_t stream)
 {
     const dim3 block(kBlockThreads);
 #define GCQ_GC2(NT)                                                                            \
     gc2_quantize_kernel<U, NT, Table, false>                                                   \
-        <<<grid, block, 0, stream>>>(one, table, nb, total_tiles, tpb, nullptr, 0.0f)
+        <<<grid, block, pad, stream>>>(one, table, nb, total_tiles, tpb, nullptr, 0.0f)
     switch (nt) {
     case 0: GCQ_GC2(0); break;
     case 1: GCQ_GC2(1); break;
@@ -254,10 +254,11 @@ hipError_t launch(const gcq_tuning &tu, const Gc2Desc &one, const Gc2Desc *table
                   uint64_t total_tiles, uint32_t tpb, hipStream_t stream)
 {
     const uint32_t grid = grid_for(total_tiles, tu.gc2_blocks_per_cu);
+    const uint32_t pad = resident_lds_pad(0, tu.gc2_resident_per_cu);
     switch (tu.gc2_unroll) {
-    case 1: launch_nt<1, Table>(tu.gc2_nt, grid, one, table, nb, total_tiles, tpb, stream); break;
-    case 2: launch_nt<2, Table>(tu.gc2_nt, grid, one, table, nb, total_tiles, tpb, stream); break;
-    default: launch_nt<4, Table>(tu.gc2_nt, grid, one, table, nb, total_tiles, tpb, stream); break;
+    case 1: launch_nt<1, Table>(tu.gc2_nt, grid, pad, one, table, nb, total_tiles, tpb, stream); break;
+    case 2: launch_nt<2, Table>(tu.gc2_nt, grid, pad, one, table, nb, total_tiles, tpb, stream); break;
+    default: launch_nt<4, Table>(tu.gc2_nt, grid, pad, one, table, nb, total_tiles, tpb, stream); break;
     }
     return hipGetLastError();
 }
@@ -300,32 +301,66 @@ __global__ __launch_bounds__(kBlockThreads) void local_update_kernel(const float
 // and its non-temporal mask reduced to none (0), all (15) or the default
 // set (g, r and w loads, r and w stores: 7).
 template <int U, int NT>
-void launch_cdsgd_u(bool quant, uint32_t grid, const Gc2Desc &one, float *w, float eta,
-                    uint64_t tiles, hipStream_t stream)
+void launch_cdsgd_u(bool quant, uint32_t grid, uint32_t pad, const Gc2Desc &one, float *w,
+                    float eta, uint64_t tiles, hipStream_t stream)
 {
     if (quant)
         gc2_quantize_kernel<U, NT, false, true>
-            <<<grid, kBlockThreads, 0, stream>>>(one, nullptr, 1, tiles, 0, w, eta);
+            <<<grid, kBlockThreads, pad, stream>>>(one, nullptr, 1, tiles, 0, w, eta);
     else
         local_update_kernel<U, NT>
-            <<<grid, kBlockThreads, 0, stream>>>(one.g, w, one.n, tiles, eta);
+            <<<grid, kBlockThreads, pad, stream>>>(one.g, w, one.n, tiles, eta);
 }
 
 template <int U>
-void launch_cdsgd_nt(int nt, bool quant, uint32_t grid, const Gc2Desc &one, float *w, float eta,
-                     uint64_t tiles, hipStream_t stream)
+void launch_cdsgd_nt(int nt, bool quant, uint32_t grid, uint32_t pad, const Gc2Desc &one,
+                     float *w, float eta, uint64_t tiles, hipStream_t stream)
 {
     if (nt == 0)
-        launch_cdsgd_u<U, 0>(quant, grid, one, w, eta, tiles, stream);
+        launch_cdsgd_u<U, 0>(quant, grid, pad, one, w, eta, tiles, stream);
     else if (nt == 15)
-        launch_cdsgd_u<U, 15>(quant, grid, one, w, eta, tiles, stream);
+        launch_cdsgd_u<U, 15>(quant, grid, pad, one, w, eta, tiles, stream);
     else
-        launch_cdsgd_u<U, 7>(quant, grid, one, w, eta, tiles, stream);
+        launch_cdsgd_u<U, 7>(quant, grid, pad, one, w, eta, tiles, stream);
+}
+
+// Writes descriptors that arrive by value in the kernel arguments into a
+// device table: one launch per kFillChunk descriptors, thread i storing
+// descriptor i.  Nothing is staged in host memory, so the caller's array may
+// be reused as soon as the launch call returns, and a table slot is ordered
+// against its earlier readers on the device alone.
+struct Gc2FillChunk {
+    Gc2Desc d[kFillChunk];
+};
+
+__global__ __launch_bounds__(kFillChunk) void gc2_table_fill_kernel(Gc2FillChunk chunk,
+                                                                     Gc2Desc *__restrict__ dst,
+                                                                     uint32_t count)
+{
+    const uint32_t i = threadIdx.x;
+    if (i < count)
+        dst[i] = chunk.d[i];
 }
 
 }  // namespace
 
 uint64_t gc2_tile_elems(const gcq_tuning &tu) { return 1024u * (uint64_t)tu.gc2_unroll; }
+
+hipError_t launch_gc2_table_fill(const Gc2Desc *descs, uint32_t count, Gc2Desc *dev_table,
+                                 hipStream_t stream)
+{
+    for (uint32_t b0 = 0; b0 < count; b0 += kFillChunk) {
+        const uint32_t c = count - b0 < kFillChunk ? count - b0 : kFillChunk;
+        Gc2FillChunk chunk = {};
+        for (uint32_t i = 0; i < c; ++i)
+            chunk.d[i] = descs[b0 + i];
+        gc2_table_fill_kernel<<<1, kFillChunk, 0, stream>>>(chunk, dev_table + b0, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream)
 {
@@ -347,10 +382,11 @@ hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint6
         return hipSuccess;
     const Gc2Desc one = {g, r, out, n, 0, t, 0};
     const uint32_t grid = grid_for(tiles, tu.gc2_blocks_per_cu);
+    const uint32_t pad = resident_lds_pad(0, tu.gc2_resident_per_cu);
     switch (tu.gc2_unroll) {
-    case 1: launch_cdsgd_nt<1>(tu.gc2_nt, quant, grid, one, w, eta, tiles, stream); break;
-    case 2: launch_cdsgd_nt<2>(tu.gc2_nt, quant, grid, one, w, eta, tiles, stream); break;
-    default: launch_cdsgd_nt<4>(tu.gc2_nt, quant, grid, one, w, eta, tiles, stream); break;
+    case 1: launch_cdsgd_nt<1>(tu.gc2_nt, quant, grid, pad, one, w, eta, tiles, stream); break;
+    case 2: launch_cdsgd_nt<2>(tu.gc2_nt, quant, grid, pad, one, w, eta, tiles, stream); break;
+    default: launch_cdsgd_nt<4>(tu.gc2_nt, quant, grid, pad, one, w, eta, tiles, stream); break;
     }
     return hipGetLastError();
 }

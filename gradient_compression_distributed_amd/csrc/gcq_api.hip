@@ -31,11 +31,12 @@ Range range(const void *p, size_t bytes, bool writable)
 // a pair (A before B in start order) overlaps iff B.lo < A.hi, so it is
 // enough to track the largest end so far among writable and among all
 // ranges.  Read-only ranges may overlap one another.
-bool any_write_overlap(std::vector<Range> &rs)
+bool any_write_overlap(Range *first, Range *last)
 {
-    std::sort(rs.begin(), rs.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    std::sort(first, last, [](const Range &a, const Range &b) { return a.lo < b.lo; });
     uintptr_t end_all = 0, end_w = 0;
-    for (const Range &r : rs) {
+    for (const Range *p = first; p != last; ++p) {
+        const Range &r = *p;
         if (r.hi == r.lo)
             continue;
         if (r.lo < end_w || (r.writable && r.lo < end_all))
@@ -47,6 +48,16 @@ bool any_write_overlap(std::vector<Range> &rs)
     return false;
 }
 
+bool any_write_overlap(std::vector<Range> &rs) { return any_write_overlap(rs.data(), rs.data() + rs.size()); }
+
+// A fixed array that check_gc2 appends to (for the path that allocates
+// nothing, not even host memory).
+struct RangeArray {
+    Range *p;
+    size_t n;
+    void push_back(const Range &r) { p[n++] = r; }
+};
+
 bool valid_threshold(float t) { return isfinite(t) && t > 0.0f; }
 
 bool valid_rate(float eta) { return isfinite(eta) && eta >= 0.0f; }
@@ -56,8 +67,9 @@ bool valid_rate(float eta) { return isfinite(eta) && eta >= 0.0f; }
 // range's end address wraps.
 constexpr size_t kMaxElems = GCQ_MAX_ELEMS;
 
+template <class Ranges>
 int check_gc2(const float *g, const float *r, size_t n, float t, const uint32_t *out,
-              std::vector<Range> *ranges)
+              Ranges *ranges)
 {
     if (!valid_threshold(t))
         return GCQ_ERR_THRESHOLD;
@@ -85,24 +97,28 @@ int launch_status(hipError_t e)
 }
 
 // Device tables of the fused launch: per device a cache of slots, each a
-// pinned host copy of the table, a device buffer and an event recorded
-// after the last kernel that read it.  A call whose descriptors match a
-// slot's reuses that slot's device table; a new table goes to the least
-// recently used slot, rewritten only once its event has completed, so a
-// call never overwrites a table still in use.  The copy and the kernel are
-// ordered on the caller's stream.  All slots are allocated together on the
-// first call (and again only when a call has more buckets than they hold).
+// device buffer, a host record of the descriptors it holds (to recognise a
+// repeated bucket list) and an event recorded after the last kernel that
+// read it.  A call whose descriptors match a slot's reuses that slot's
+// table.  A new table goes to the least recently used slot.  Either way the
+// caller's stream first waits, on the device, for the slot's event, so a
+// table is read only after its fill and rewritten only after its last
+// reader, whatever streams they ran on; the host never waits.  The fill is a
+// kernel whose arguments carry the descriptors (nothing is staged in host
+// memory).  All slots are allocated together on the first call; a call with
+// more buckets than they hold grows them, which is the one case where the
+// host waits (for the kernels still reading the old buffers) and device
+// memory is allocated.
 constexpr int kRing = 8;
 constexpr int kMaxDevices = 64;
 
 struct Slot {
-    Gc2Desc *host = nullptr;
+    std::vector<Gc2Desc> descs;  // the table it holds (empty: none)
     Gc2Desc *dev = nullptr;
     size_t cap = 0;
-    size_t count = 0;       // descriptors of the table it holds (0: none)
-    uint64_t used = 0;      // call number of its last use
+    uint64_t used = 0;           // call number of its last use
     hipEvent_t ev = nullptr;
-    bool pending = false;
+    bool pending = false;        // ev recorded after a kernel that read the table
 };
 
 struct DeviceRing {
@@ -113,31 +129,61 @@ struct DeviceRing {
 
 DeviceRing g_rings[kMaxDevices];
 
-// A slot able to hold nb descriptors.  Growing frees the old buffers, so
-// the slot's last kernel must have completed (the caller waits for it).
+// A slot able to hold nb descriptors.  Growing frees the old buffer, so the
+// host first waits for the slot's last reader.
 int ensure_capacity(Slot &s, size_t nb)
 {
     if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
         return GCQ_ERR_NOMEM;
     if (s.cap >= nb)
         return GCQ_OK;
+    if (s.pending) {
+        if (hipEventSynchronize(s.ev) != hipSuccess)
+            return GCQ_ERR_LAUNCH;
+        s.pending = false;
+    }
     size_t cap = std::max<size_t>(nb, 2 * s.cap);
-    if (s.host)
-        (void)hipHostFree(s.host);
     if (s.dev)
         (void)hipFree(s.dev);
-    s.host = nullptr;
     s.dev = nullptr;
     s.cap = 0;
-    s.count = 0;
-    if (hipHostMalloc((void **)&s.host, cap * sizeof(Gc2Desc), hipHostMallocDefault) != hipSuccess)
+    s.descs.clear();
+    if (hipMalloc((void **)&s.dev, cap * sizeof(Gc2Desc)) != hipSuccess)
         return GCQ_ERR_NOMEM;
-    if (hipMalloc((void **)&s.dev, cap * sizeof(Gc2Desc)) != hipSuccess) {
-        (void)hipHostFree(s.host);
-        s.host = nullptr;
-        return GCQ_ERR_NOMEM;
-    }
     s.cap = cap;
+    return GCQ_OK;
+}
+
+// Checks every bucket of a fused call and builds its device descriptors:
+// ranges receives up to 3 per bucket, descs one per bucket.  tpb is the
+// tile count shared by every bucket (0 if they differ): the kernel then
+// finds a tile's bucket by one division.
+int prepare_buckets(const gc2_bucket *buckets, uint32_t num_buckets, const gcq_tuning &tu,
+                    RangeArray *ranges, Gc2Desc *descs, uint64_t *total_tiles, uint64_t *tpb)
+{
+    uint64_t tiles_total = 0, total_elems = 0;
+    const uint64_t te = gcq::gc2_tile_elems(tu);
+    uint64_t same = (buckets[0].n + te - 1) / te;
+    for (uint32_t b = 0; b < num_buckets; ++b) {
+        const gc2_bucket &k = buckets[b];
+        int st = check_gc2(k.g, k.r, k.n, k.t, k.out_words, ranges);
+        if (st != GCQ_OK)
+            return st;
+        total_elems += k.n;   // each term <= 2^60, checked as it grows: no wrap
+        if (total_elems > kMaxElems)
+            return GCQ_ERR_PARAM;
+        const uint64_t tiles = (k.n + te - 1) / te;
+        if (tiles != same)
+            same = 0;
+        descs[b] = Gc2Desc{k.g, k.r, k.out_words, (uint64_t)k.n, tiles_total, k.t, 0};
+        tiles_total += tiles;
+    }
+    if (same > 0xFFFFFFFFu)
+        same = 0;
+    if (any_write_overlap(ranges->p, ranges->p + ranges->n))
+        return GCQ_ERR_OVERLAP;
+    *total_tiles = tiles_total;
+    *tpb = same;
     return GCQ_OK;
 }
 
@@ -204,44 +250,18 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         return GCQ_ERR_NULL;
     if (num_buckets > 0x7FFFFFFFu)
         return GCQ_ERR_PARAM;
-    std::vector<Range> ranges;
-    ranges.reserve(3 * (size_t)num_buckets);
-    uint64_t total_tiles = 0, total_elems = 0;
-    // every bucket spanning the same number of tiles lets the kernel find a
-    // tile's bucket by one division
+    std::vector<Range> ranges(3 * (size_t)num_buckets);
+    std::vector<Gc2Desc> descs(num_buckets);
     const gcq_tuning tu = gcq::tuning();
-    const uint64_t te = gcq::gc2_tile_elems(tu);
-    uint64_t tpb = (buckets[0].n + te - 1) / te;
-    for (uint32_t b = 0; b < num_buckets; ++b) {
-        const gc2_bucket &k = buckets[b];
-        int st = check_gc2(k.g, k.r, k.n, k.t, k.out_words, &ranges);
-        if (st != GCQ_OK)
-            return st;
-        total_elems += k.n;   // each term <= 2^60, checked as it grows: no wrap
-        if (total_elems > kMaxElems)
-            return GCQ_ERR_PARAM;
-        const uint64_t tiles = (k.n + te - 1) / te;
-        if (tiles != tpb)
-            tpb = 0;
-        total_tiles += tiles;
-    }
-    if (tpb > 0xFFFFFFFFu)
-        tpb = 0;
-    if (any_write_overlap(ranges))
-        return GCQ_ERR_OVERLAP;
-    if (total_tiles == 0)
-        return GCQ_OK;
+    RangeArray ra{ranges.data(), 0};
+    uint64_t total_tiles = 0, tpb = 0;
+    int st = prepare_buckets(buckets, num_buckets, tu, &ra, descs.data(), &total_tiles, &tpb);
+    if (st != GCQ_OK || total_tiles == 0)
+        return st;
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return GCQ_ERR_LAUNCH;
-    std::vector<Gc2Desc> descs(num_buckets);
-    uint64_t tile = 0;
-    for (uint32_t b = 0; b < num_buckets; ++b) {
-        const gc2_bucket &k = buckets[b];
-        descs[b] = Gc2Desc{k.g, k.r, k.out_words, (uint64_t)k.n, tile, k.t, 0};
-        tile += (k.n + te - 1) / te;
-    }
     const size_t bytes = num_buckets * sizeof(Gc2Desc);
     hipStream_t hs = (hipStream_t)stream;
     DeviceRing &ring = g_rings[dev];
@@ -249,60 +269,43 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
     ++ring.calls;
     // The same buckets as an earlier call (the usual case: fusion buckets are
     // fixed across training steps, possibly a few alternating sets): the
-    // table already on the device is reused as is.  The stream first waits
-    // for the slot's event (recorded after the last kernel that read the
-    // table, itself after the upload), so the upload is complete whatever
-    // stream made it, and the event then re-recorded covers every kernel that
-    // used the slot: a slot is only rewritten once all of them have finished.
+    // table already on the device is reused as is.
     Slot *sp = nullptr;
     for (Slot &c : ring.slots) {
-        if (c.count == num_buckets && memcmp(c.host, descs.data(), bytes) == 0) {
+        if (c.descs.size() == num_buckets && memcmp(c.descs.data(), descs.data(), bytes) == 0) {
             sp = &c;
             break;
         }
     }
-    if (sp) {
-        if (sp->pending && hipStreamWaitEvent(hs, sp->ev, 0) != hipSuccess)
-            return GCQ_ERR_LAUNCH;
-    } else {
+    bool fill = false;
+    if (!sp) {
         Slot *lru = &ring.slots[0];
         for (Slot &c : ring.slots)
             if (c.used < lru->used)
                 lru = &c;
-        Slot &s = *lru;
-        if (s.pending) {
-            if (hipEventSynchronize(s.ev) != hipSuccess)
-                return GCQ_ERR_LAUNCH;
-            s.pending = false;
-        }
-        s.count = 0;
-        if (s.cap < num_buckets) {
-            // every free slot grows with it, so later new tables of this size
+        if (lru->cap < num_buckets) {
+            // every slot grows with it, so later new tables of this size
             // allocate nothing
             for (Slot &c : ring.slots) {
-                if (c.cap >= num_buckets)
-                    continue;
-                if (c.pending) {
-                    if (hipEventSynchronize(c.ev) != hipSuccess)
-                        return GCQ_ERR_LAUNCH;
-                    c.pending = false;
-                }
                 int st = ensure_capacity(c, num_buckets);
                 if (st != GCQ_OK)
                     return st;
             }
         }
-        int st = ensure_capacity(s, num_buckets);
-        if (st != GCQ_OK)
-            return st;
-        memcpy(s.host, descs.data(), bytes);
-        if (hipMemcpyAsync(s.dev, s.host, bytes, hipMemcpyHostToDevice, hs) != hipSuccess)
-            return GCQ_ERR_LAUNCH;
-        s.count = num_buckets;
-        sp = &s;
+        sp = lru;
+        sp->descs.clear();
+        fill = true;
     }
-    sp->used = ring.calls;
     Slot &s = *sp;
+    if (s.pending && hipStreamWaitEvent(hs, s.ev, 0) != hipSuccess)
+        return GCQ_ERR_LAUNCH;
+    if (fill) {
+        hipError_t e = gcq::launch_gc2_table_fill(descs.data(), num_buckets, s.dev, hs);
+        if (e != hipSuccess)
+            return launch_status(e);
+        s.descs = std::move(descs);
+    }
+    s.used = ring.calls;
     hipError_t e = gcq::launch_gc2_table(tu, s.dev, num_buckets, total_tiles, (uint32_t)tpb, hs);
     if (e != hipSuccess)
         return launch_status(e);
@@ -351,8 +354,11 @@ int cdsgd_local_update(const float *g, float *w_loc, size_t n, float eta, void *
                                            (hipStream_t)stream));
 }
 
-int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t, float *acc,
-                       void *stream)
+namespace {
+
+// The reduce's checks and launch; probe = true runs gcq_probe_reduce.
+int dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t, float *acc,
+                   void *stream, bool probe)
 {
     if (W == 0 || W > GCQ_MAX_WORKERS)
         return GCQ_ERR_PARAM;
@@ -381,7 +387,43 @@ int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float
     ranges.push_back(range(acc, n * 4, true));
     if (any_write_overlap(ranges))
         return GCQ_ERR_OVERLAP;
-    return launch_status(gcq::launch_dequant_reduce(ws, W, n, t, acc, (hipStream_t)stream));
+    return launch_status(gcq::launch_dequant_reduce(ws, W, n, t, acc, (hipStream_t)stream, probe));
+}
+
+}  // namespace
+
+int gc2_dequant_reduce(const uint32_t *const *words, uint32_t W, size_t n, float t, float *acc,
+                       void *stream)
+{
+    return dequant_reduce(words, W, n, t, acc, stream, false);
+}
+
+int gcq_probe_reduce(const uint32_t *const *words, uint32_t W, size_t n, float *acc, void *stream)
+{
+    return dequant_reduce(words, W, n, 1.0f, acc, stream, true);
+}
+
+int gcq_probe_stream(const float *a, const float *b, float *c, uint32_t *words, size_t n,
+                     void *stream)
+{
+    if (n > kMaxElems || n % 1024 != 0)
+        return GCQ_ERR_PARAM;
+    if (n == 0)
+        return GCQ_OK;
+    if (!a || !c)
+        return GCQ_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(c, 16) || (b && !aligned(b, 16)) || (words && !aligned(words, 4)))
+        return GCQ_ERR_ALIGN;
+    std::vector<Range> ranges;
+    ranges.push_back(range(a, n * 4, false));
+    if (b && b != c)   // c may be b itself: in place, as the quantizer updates r
+        ranges.push_back(range(b, n * 4, false));
+    ranges.push_back(range(c, n * 4, true));
+    if (words)
+        ranges.push_back(range(words, n / 16 * 4, true));
+    if (any_write_overlap(ranges))
+        return GCQ_ERR_OVERLAP;
+    return launch_status(gcq::launch_probe_stream(a, b, c, words, n, (hipStream_t)stream));
 }
 
 static int qsgd_quantize_impl(const float *g, size_t n, uint32_t d, uint32_t s, uint64_t seed,

@@ -34,6 +34,17 @@ __device__ __forceinline__ void st(P p, T v)
         *p = v;
 }
 
+// Buffer resources and cache-policy bits (gfx950): word 3 of a raw
+// (stride 0, byte-addressed) buffer resource, and the aux bits of the
+// buffer load/store builtins: sc0 1, nt 2, sc1 16.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCpolSc0 = 1;
+constexpr int kCpolNt = 2;
+constexpr int kCpolSc1 = 16;
+
+// LDS per compute unit on gfx950.
+constexpr uint32_t kLdsBytesPerCu = 160u * 1024u;
+
 // DPP quad permutes (within each aligned group of 4 lanes): broadcast lane
 // q, or swap neighbouring lanes.  All lanes must be active.
 template <int Ctrl>

@@ -51,6 +51,14 @@ bool tuning_valid(const gcq_tuning &t);
 // Number of compute units of the current device (cached per device).
 int device_cus();
 
+// Dynamic LDS (bytes, never touched by the kernel) that leaves room for at
+// most `resident` workgroups per compute unit when each also holds
+// `static_bytes` of its own: a cap on resident workgroups set through the
+// LDS allocation.  0: no cap.  Fewer resident workgroups keep fewer read and
+// write windows open in HBM at once, which the streaming kernels measured
+// faster at some settings (the launch knobs choose).
+uint32_t resident_lds_pad(uint32_t static_bytes, int resident);
+
 // Grid size for `work_blocks` workgroups of work: all of them when
 // blocks_per_cu == 0, else at most blocks_per_cu per compute unit (the
 // kernel then strides); clamped to [1, 2^31 - 1].
@@ -66,6 +74,12 @@ hipError_t launch_gc2_single(const Gc2Desc &one, hipStream_t stream);
 // (the kernel then finds its bucket by a division instead of a search).
 hipError_t launch_gc2_table(const gcq_tuning &tu, const Gc2Desc *dev_table, uint32_t nbuckets,
                             uint64_t total_tiles, uint32_t tiles_per_bucket, hipStream_t stream);
+// Copies count host descriptors into the device table with small kernels
+// whose arguments carry the descriptors (kFillChunk per launch), ordered on
+// `stream`; the host array is not referenced after the call returns.
+constexpr uint32_t kFillChunk = 64;
+hipError_t launch_gc2_table_fill(const Gc2Desc *descs, uint32_t count, Gc2Desc *dev_table,
+                                 hipStream_t stream);
 // CD-SGD local update (Quant = false) or update fused with the quantizer.
 hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint64_t n, float t,
                         float eta, bool quant, hipStream_t stream);
@@ -84,8 +98,13 @@ hipError_t launch_saps_mask(uint64_t n, float c, uint64_t seed, uint32_t *mask, 
                             hipStream_t stream);
 hipError_t launch_saps_apply(float *x, uint64_t n, const uint32_t *mask, const uint64_t *offs,
                              float *values, uint64_t cap, bool merge, hipStream_t stream);
+// probe: the same kernel and launch with the decode replaced by an XOR of
+// the words (gcq_probe_reduce).
 hipError_t launch_dequant_reduce(const DqWorkers &w, uint32_t W, uint64_t n, float t,
-                                 float *acc, hipStream_t stream);
+                                 float *acc, hipStream_t stream, bool probe = false);
+// The streaming probe (gcq_probe_stream).
+hipError_t launch_probe_stream(const float *a, const float *b, float *c, uint32_t *words,
+                               uint64_t n, hipStream_t stream);
 // maxnorm: bucket scale = largest magnitude (else the L2 norm).
 hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t s, uint64_t seed,
                                 float *norms, uint32_t *nibbles, bool maxnorm, hipStream_t stream);

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "gcq_device.h"
 #include "gcq_internal.h"
 
 namespace gcq {
@@ -23,6 +24,8 @@ int env_int(const char *name, int dflt)
 }
 
 int env_flag(const char *name, int dflt) { return env_int(name, dflt) ? 1 : 0; }
+
+bool resident_ok(int v) { return v == 0 || (v >= 2 && v <= 8); }
 
 int env_count(const char *name, int dflt)
 {
@@ -54,6 +57,12 @@ void init_locked()
         g_tuning.qsgd_buckets_per_wave != 4)
         g_tuning.qsgd_buckets_per_wave = 0;
     g_tuning.dq_words_per_thread = env_int("GCQ_DQ_WORDS_PER_THREAD", 2) == 1 ? 1 : 2;
+    g_tuning.dq_resident_per_cu = env_int("GCQ_DQ_RESIDENT_PER_CU", 3);
+    if (!resident_ok(g_tuning.dq_resident_per_cu))
+        g_tuning.dq_resident_per_cu = 3;
+    g_tuning.gc2_resident_per_cu = env_int("GCQ_GC2_RESIDENT_PER_CU", 0);
+    if (!resident_ok(g_tuning.gc2_resident_per_cu))
+        g_tuning.gc2_resident_per_cu = 0;
     g_init = true;
 }
 
@@ -78,7 +87,8 @@ bool tuning_valid(const gcq_tuning &t)
            count_ok(t.qsgd_dequant_blocks_per_cu) &&
            (t.qsgd_buckets_per_wave == 0 || t.qsgd_buckets_per_wave == 1 ||
             t.qsgd_buckets_per_wave == 2 || t.qsgd_buckets_per_wave == 4) &&
-           (t.dq_words_per_thread == 1 || t.dq_words_per_thread == 2);
+           (t.dq_words_per_thread == 1 || t.dq_words_per_thread == 2) &&
+           resident_ok(t.dq_resident_per_cu) && resident_ok(t.gc2_resident_per_cu);
 }
 
 void set_tuning(const gcq_tuning &t)
@@ -104,6 +114,14 @@ int device_cus()
         cache[dev] = cus;
     }
     return cache[dev];
+}
+
+uint32_t resident_lds_pad(uint32_t static_bytes, int resident)
+{
+    if (resident <= 0)
+        return 0;
+    const uint32_t per = dev::kLdsBytesPerCu / (uint32_t)resident - 1024u;
+    return per > static_bytes ? per - static_bytes : 0u;
 }
 
 uint32_t grid_for(uint64_t work_blocks, int blocks_per_cu)

@@ -28,8 +28,12 @@
  *     reference to them after the call.  Host arrays are marked "host".
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *     call only enqueues work on that stream and returns; it never
- *     synchronizes.  Faults during execution surface at the caller's next
- *     synchronization with the stream.
+ *     synchronizes, with one exception: a gc2_quantize_buckets call with
+ *     more buckets than any earlier call on the device grows the library's
+ *     device tables, which allocates device memory and first waits on the
+ *     host for the kernels still reading the old tables.  Faults during
+ *     execution surface at the caller's next synchronization with the
+ *     stream.
  *   - Every argument is checked on the host before anything is enqueued; a
  *     call that returns an error has enqueued nothing and changed nothing.
  *   - Return value: GCQ_OK (0) or a negative GCQ_ERR_* status;
@@ -116,11 +120,16 @@ typedef struct gc2_bucket {
  * its packing starts at its own out_words[0], its tail pairs are 00.
  *
  *   buckets      host array of num_buckets descriptors; read during the
- *                call only (the library copies it into a library-owned,
- *                stream-ordered device table, or reuses one of the last 8
- *                distinct tables it uploaded when the descriptors match;
- *                the tables are allocated on the first call and grown on
- *                demand)
+ *                call only.  The library writes it into one of 8 device
+ *                tables it owns per device, with small kernels whose
+ *                arguments carry the descriptors, or reuses a table it
+ *                already holds when the descriptors match.  The caller's
+ *                stream waits on the device for the table's earlier
+ *                readers, so calls on different streams may share tables;
+ *                the host does not wait.  The tables are allocated on the
+ *                first call and grown (with the host wait described in the
+ *                conventions above) when a call has more buckets than they
+ *                hold.
  *   num_buckets  0 .. 2^31-1
  *   stream       hipStream_t
  *
@@ -395,11 +404,16 @@ int saps_merge(float *x, size_t n, const uint32_t *mask_words, const uint64_t *t
 /* Sizes and status names (pure host functions, no device access)      */
 /* ------------------------------------------------------------------ */
 
-/* ceil(n/16): packed 2-bit words for n elements (MXNet PR: 1/16 the size). */
+/* ceil(n/16): packed 2-bit words for n elements (MXNet PR, "Format of
+ * compressed gradient": 16 codes per 32-bit element, 1/16 the size). */
 size_t gc2_packed_words(size_t n);
-/* ceil(n/d): QSGD buckets (d >= 1; returns 0 for d == 0). */
+/* ceil(n/d): QSGD buckets of d consecutive coordinates, the last one ragged
+ * (QSGD summary, Knowl 8: the vector is split into buckets of size d, each
+ * quantized with its own scale); returns 0 for d == 0. */
 size_t qsgd_num_buckets(size_t n, uint32_t d);
-/* ceil(n/8): QSGD nibble words. */
+/* ceil(n/8): 32-bit words of the nibble stream.  Knowl 2 sends a sign and a
+ * level per coordinate; with s <= 7 both fit one 4-bit nibble (bit 3 the
+ * sign, bits 2..0 the level), 8 per word. */
 size_t qsgd_nibble_words(size_t n);
 /* An upper bound of the words qsgd_elias_encode writes (0 for a bad d). */
 size_t qsgd_elias_max_words(size_t n, uint32_t d);
@@ -409,6 +423,39 @@ size_t saps_mask_words(size_t n);
 size_t saps_num_tiles(size_t n);
 /* Static, never-NULL name of a status code. */
 const char *gcq_status_string(int status);
+
+/* ------------------------------------------------------------------ */
+/* Measurement probes (not part of the method)                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Kernels with a hot-path kernel's HBM access pattern and none of its
+ * arithmetic.  Timed beside that kernel they give the practical ceiling of
+ * its access pattern on the device at hand, against which its own time is
+ * judged (the 8 TB/s HBM peak is not reachable by any access pattern).
+ *
+ * gcq_probe_stream -- the 2-bit quantizer's pattern (its default launch
+ * geometry, 1024 elements per 256-thread workgroup, one float4 per lane
+ * and stream): reads a (and b, unless NULL), writes c, and, unless words is
+ * NULL, one 32-bit word per 16 elements in 64-byte runs.  c = a XOR b bit for
+ * bit (c = a without b); word 16k + L holds the bits of c[256k + 4L] (L < 16).
+ * With a, b, c and words it moves the quantizer's 12.25 bytes per element;
+ * with a and c alone it is a copy.
+ *   a, b, c  float32[n], 16-byte aligned; words uint32[n/16], 4-byte aligned
+ *   n        a multiple of 1024
+ * Errors: GCQ_ERR_PARAM (n), GCQ_ERR_NULL (a or c), GCQ_ERR_ALIGN,
+ * GCQ_ERR_OVERLAP (c or words intersects another operand; c may be b
+ * itself, in place, as the quantizer updates r), GCQ_ERR_LAUNCH.
+ *
+ * gcq_probe_reduce -- gc2_dequant_reduce's own kernel and launch (the same
+ * loads, LDS staging, stores, launch knobs and checks, no threshold) with
+ * the decode replaced by an XOR: acc[16i] holds the XOR of the W workers'
+ * word i, the other 15 sums of each word are +0.
+ */
+int gcq_probe_stream(const float *a, const float *b, float *c, uint32_t *words, size_t n,
+                     void *stream);
+int gcq_probe_reduce(const uint32_t *const *words, uint32_t W, size_t n, float *acc,
+                     void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Launch knobs: they change speed, never results                      */
@@ -463,6 +510,12 @@ typedef struct gcq_tuning {
     int dq_words_per_thread; /* gc2_dequant_reduce: packed words per thread,
                                1 or 2 (default: 8-byte loads, used when every
                                worker array is 8-byte aligned, else 1) */
+    int dq_resident_per_cu; /* gc2_dequant_reduce: at most this many
+                               workgroups resident per compute unit, set through
+                               the kernel's LDS allocation: 0 (no cap) or 2..8
+                               (default 3) */
+    int gc2_resident_per_cu; /* the 2-bit quantizer and the CD-SGD kernels:
+                               the same cap, 0 (no cap, default) or 2..8 */
 } gcq_tuning;
 
 /*
@@ -470,7 +523,8 @@ typedef struct gcq_tuning {
  * initial values are the library defaults, overridden by the environment
  * variables GCQ_GC2_UNROLL, GCQ_GC2_NT, GCQ_GC2_BLOCKS_PER_CU,
  * GCQ_DQ_NT_LOADS, GCQ_DQ_NT_STORES, GCQ_DQ_LDS_STORES, GCQ_DQ_FP4_DECODE,
- * GCQ_DQ_BLOCKS_PER_CU, GCQ_DQ_WORDS_PER_THREAD, GCQ_QSGD_NT, GCQ_QSGD_RCP,
+ * GCQ_DQ_BLOCKS_PER_CU, GCQ_DQ_WORDS_PER_THREAD, GCQ_DQ_RESIDENT_PER_CU,
+ * GCQ_GC2_RESIDENT_PER_CU, GCQ_QSGD_NT, GCQ_QSGD_RCP,
  * GCQ_QSGD_DEQUANT_NT, GCQ_QSGD_BLOCKS_PER_CU, GCQ_QSGD_DEQUANT_BLOCKS_PER_CU
  * and GCQ_QSGD_BUCKETS_PER_WAVE when set (block counts and gc2_nt are
  * clamped into range, a flag reads any nonzero value as 1, and any other
@@ -482,7 +536,9 @@ typedef struct gcq_tuning {
  * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
  * flag not 0/1, gc2_nt outside 0..15, gc2_unroll not 1/2/4, a block
  * count outside 0..1024, qsgd_buckets_per_wave not 0/1/2/4,
- * dq_words_per_thread not 1/2); on error nothing changes.
+ * dq_words_per_thread not 1/2, dq_resident_per_cu or gc2_resident_per_cu
+ * not 0 or 2..8); on error
+ * nothing changes.
  */
 int gcq_get_tuning(gcq_tuning *out);
 int gcq_set_tuning(const gcq_tuning *t);

@@ -102,6 +102,31 @@ def test_gc2_buckets_validation(lib):
     assert call([(0, 0, 0, 0, 0.5), (0, 0, 0, 0, 0.5)]) == OK
 
 
+def test_probe_validation(lib):
+    ps = lambda a, b, c, w, n: lib.gcq_probe_stream(vp(a), vp(b), vp(c), vp(w), n, NULL)
+    mb = 1 << 20
+    assert ps(A, 0, A + mb, 0, 0) == OK
+    assert ps(A, 0, A + mb, 0, 1000) == E_PARAM          # not a multiple of 1024
+    assert ps(0, 0, A + mb, 0, 1024) == E_NULL
+    assert ps(A, 0, 0, 0, 1024) == E_NULL
+    assert ps(A + 4, 0, A + mb, 0, 1024) == E_ALIGN
+    assert ps(A, A + 8, A + mb, 0, 1024) == E_ALIGN
+    assert ps(A, 0, A + mb, A + 2 * mb + 2, 1024) == E_ALIGN
+    assert ps(A, 0, A + 64, 0, 1024) == E_OVERLAP
+    assert ps(A, A + mb, A + 2 * mb, A + mb + 64, 1024) == E_OVERLAP
+    # c may be b itself (in place), but not overlap it partly (the accepted
+    # in-place form is exercised on a GPU, with real buffers)
+    assert ps(A, A + mb, A + mb + 16, 0, 1024) == E_OVERLAP
+    ws = (ctypes.c_void_p * 2)(A, A + mb)
+    pr = lambda W, n, acc: lib.gcq_probe_reduce(ws, W, n, vp(acc), NULL)
+    assert pr(2, 0, A + 2 * mb) == OK
+    assert pr(0, 100, A + 2 * mb) == E_PARAM
+    assert pr(65, 100, A + 2 * mb) == E_PARAM
+    assert pr(2, 100, 0) == E_NULL
+    assert pr(2, 100, A + 2 * mb + 4) == E_ALIGN
+    assert pr(2, 100, A + mb) == E_OVERLAP
+
+
 def test_cdsgd_validation(lib):
     n = 1000
     g, r, w, o = A, A + (1 << 20), A + (2 << 20), A + (3 << 20)
@@ -263,7 +288,10 @@ def test_tuning_roundtrip_and_validation(lib):
                        ("qsgd_rcp", 2), ("qsgd_dequant_nt", 3), ("dq_fp4_decode", 2),
                        ("qsgd_blocks_per_cu", -1), ("qsgd_dequant_blocks_per_cu", 1025),
                        ("qsgd_buckets_per_wave", 3), ("qsgd_buckets_per_wave", -1),
-                       ("dq_words_per_thread", 3), ("dq_words_per_thread", 0)]:
+                       ("dq_words_per_thread", 3), ("dq_words_per_thread", 0),
+                       ("dq_resident_per_cu", 1), ("dq_resident_per_cu", 9),
+                       ("dq_resident_per_cu", -1), ("gc2_resident_per_cu", 1),
+                       ("gc2_resident_per_cu", 9)]:
         b = gcq.Tuning(**saved)
         setattr(b, field, bad)
         assert lib.gcq_set_tuning(ctypes.byref(b)) == E_PARAM, field
@@ -324,7 +352,8 @@ def test_element_limit(lib):
 DEFAULTS = {"gc2_unroll": 1, "gc2_nt": 7, "gc2_blocks_per_cu": 0, "dq_nt_loads": 1,
             "dq_nt_stores": 1, "dq_lds_stores": 1, "dq_blocks_per_cu": 0, "dq_fp4_decode": 1,
             "qsgd_nt": 1, "qsgd_rcp": 1, "qsgd_dequant_nt": 1, "qsgd_blocks_per_cu": 0,
-            "qsgd_dequant_blocks_per_cu": 0, "qsgd_buckets_per_wave": 0, "dq_words_per_thread": 2}
+            "qsgd_dequant_blocks_per_cu": 0, "qsgd_buckets_per_wave": 0, "dq_words_per_thread": 2,
+            "dq_resident_per_cu": 3, "gc2_resident_per_cu": 0}
 
 
 def _fresh_tuning(extra_env):
@@ -349,7 +378,10 @@ def test_tuning_defaults_and_environment():
         assert knob in header, knob
         assert "GCQ_" + knob.upper() in header, knob
     t = _fresh_tuning({"GCQ_DQ_WORDS_PER_THREAD": "1", "GCQ_GC2_NT": "99",
-                       "GCQ_QSGD_BUCKETS_PER_WAVE": "3", "GCQ_DQ_BLOCKS_PER_CU": "5"})
+                       "GCQ_QSGD_BUCKETS_PER_WAVE": "3", "GCQ_DQ_BLOCKS_PER_CU": "5",
+                       "GCQ_DQ_RESIDENT_PER_CU": "1"})
+    assert t["dq_resident_per_cu"] == 3            # invalid: the default
+    assert _fresh_tuning({"GCQ_DQ_RESIDENT_PER_CU": "0"})["dq_resident_per_cu"] == 0
     assert t["dq_words_per_thread"] == 1
     assert t["gc2_nt"] == 15                       # clamped into 0..15
     assert t["qsgd_buckets_per_wave"] == 0         # invalid: the default

@@ -29,17 +29,17 @@ def test_more_than_one_gpu_is_refused(argv, env):
 def test_arena_views_are_aligned_and_disjoint():
     import torch
 
-    layout = [(1000, torch.float32), (3, torch.int32), (4097, torch.float32), (1, torch.int64),
-              (0, torch.float32), (65, torch.int32)]
+    layout = [(1000, torch.float32, 0), (3, torch.int32, 4096), (4097, torch.float32, 0),
+              (1, torch.int64, 28672), (0, torch.float32, 0), (65, torch.int32, 8192)]
     views = bench.arena(layout, "cpu")
     base = views[0].untyped_storage().data_ptr()
     spans = []
-    for v, (numel, dt) in zip(views, layout):
+    for v, (numel, dt, phase) in zip(views, layout):
         assert v.dtype == dt and v.numel() == numel and v.is_contiguous()
         if numel == 0:                 # an empty view has no address to check
             continue
         start = v.data_ptr() - base
-        assert start % 4096 == 0
+        assert start % 4096 == 0 and start % bench.PHASE == phase
         spans.append((start, start + numel * v.element_size()))
     spans.sort()
     for (a0, a1), (b0, _) in zip(spans, spans[1:]):

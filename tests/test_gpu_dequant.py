@@ -44,13 +44,14 @@ def test_w16_resnet50_sized(gpu):
 
 
 DQ_VARIANTS = [dict(dq_nt_loads=l, dq_nt_stores=s, dq_lds_stores=d, dq_blocks_per_cu=b,
-                    dq_fp4_decode=f, dq_words_per_thread=k)
-               for (l, s, d, b, f, k) in [(1, 1, 1, 0, 1, 1), (1, 0, 0, 0, 1, 1),
-                                          (0, 1, 1, 4, 0, 1), (0, 0, 0, 2, 1, 1),
-                                          (1, 1, 0, 0, 0, 1), (0, 0, 1, 1, 1, 1),
-                                          (1, 1, 1, 8, 0, 1), (0, 1, 0, 0, 1, 1),
-                                          (1, 1, 1, 0, 1, 2), (0, 0, 1, 3, 0, 2),
-                                          (1, 0, 1, 0, 1, 2), (0, 1, 1, 0, 0, 2)]]
+                    dq_fp4_decode=f, dq_words_per_thread=k, dq_resident_per_cu=c)
+               for (l, s, d, b, f, k, c) in [(1, 1, 1, 0, 1, 1, 2), (1, 0, 0, 0, 1, 1, 0),
+                                             (0, 1, 1, 4, 0, 1, 3), (0, 0, 0, 2, 1, 1, 2),
+                                             (1, 1, 0, 0, 0, 1, 8), (0, 0, 1, 1, 1, 1, 0),
+                                             (1, 1, 1, 8, 0, 1, 2), (0, 1, 0, 0, 1, 1, 4),
+                                             (1, 1, 1, 0, 1, 2, 2), (0, 0, 1, 3, 0, 2, 0),
+                                             (1, 0, 1, 0, 1, 2, 3), (0, 1, 1, 0, 0, 2, 8),
+                                             (1, 1, 1, 0, 1, 2, 0), (1, 1, 1, 2, 1, 2, 2)]]
 
 
 @pytest.mark.parametrize("var", range(len(DQ_VARIANTS)))
@@ -105,3 +106,38 @@ def test_roundtrip_with_gpu_quantizer(gpu):
         words_h.append(oracle.gc2_quantize(g, np.zeros(n, np.float32), t))
     acc = gpu.gc2_dequant_reduce(words_d, n, t)
     assert np.array_equal(bits(host(acc)), bits(oracle.gc2_dequant_reduce(words_h, n, t)))
+
+
+def test_probes_compute_what_they_state(gpu):
+    # the measurement probes keep every load and store (their outputs are
+    # defined): the reduce probe's acc[16 i] is the XOR of the workers'
+    # word i and its other sums +0; the stream probe's c is a XOR b and its
+    # word 16k + L the bits of c[256k + 4L]
+    import torch
+
+    say("probes")
+    rs = np.random.default_rng(41)
+    for n, W in ((16 * 4096 + 7, 16), (1 << 20, 5)):
+        nw = oracle.packed_words(n)
+        ws = [rs.integers(0, 1 << 32, nw, dtype=np.uint64).astype(np.uint32) for _ in range(W)]
+        acc = torch.full((n,), 3.0, device="cuda")
+        gpu.probe_reduce([dev(w) for w in ws], n, acc)
+        got = host(acc).view(np.uint32)
+        x = np.bitwise_xor.reduce(np.stack(ws), axis=0)
+        want = np.zeros(nw * 16, np.uint32)
+        want[::16] = x
+        assert np.array_equal(got, want[:n]), (n, W)
+    n = 1 << 20
+    a = dev(rs.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)).view(torch.float32)
+    b = dev(rs.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)).view(torch.float32)
+    c = torch.empty(n, device="cuda")
+    words = torch.empty(n // 16, dtype=torch.int32, device="cuda")
+    gpu.probe_stream(a, c, b=b, words=words)
+    ah, bh, ch = (host(t).view(np.uint32) for t in (a, b, c))
+    assert np.array_equal(ch, ah ^ bh)
+    k = np.arange(n // 16)
+    assert np.array_equal(host(words), ch[(k // 16) * 256 + 4 * (k % 16)])
+    gpu.probe_stream(a, c)
+    assert np.array_equal(host(c).view(np.uint32), ah)
+    gpu.probe_stream(a, b, b=b, words=words)          # in place, as the quantizer updates r
+    assert np.array_equal(host(b).view(np.uint32), ah ^ bh)

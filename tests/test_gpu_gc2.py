@@ -36,12 +36,13 @@ def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-VARIANTS = [dict(gc2_unroll=1, gc2_nt=7, gc2_blocks_per_cu=0),
-            dict(gc2_unroll=2, gc2_nt=15, gc2_blocks_per_cu=0),
-            dict(gc2_unroll=4, gc2_nt=0, gc2_blocks_per_cu=8),
-            dict(gc2_unroll=1, gc2_nt=0, gc2_blocks_per_cu=2),
-            dict(gc2_unroll=4, gc2_nt=5, gc2_blocks_per_cu=0),
-            dict(gc2_unroll=2, gc2_nt=10, gc2_blocks_per_cu=3)]
+VARIANTS = [dict(gc2_unroll=1, gc2_nt=7, gc2_blocks_per_cu=0, gc2_resident_per_cu=0),
+            dict(gc2_unroll=2, gc2_nt=15, gc2_blocks_per_cu=0, gc2_resident_per_cu=3),
+            dict(gc2_unroll=4, gc2_nt=0, gc2_blocks_per_cu=8, gc2_resident_per_cu=0),
+            dict(gc2_unroll=1, gc2_nt=0, gc2_blocks_per_cu=2, gc2_resident_per_cu=8),
+            dict(gc2_unroll=4, gc2_nt=5, gc2_blocks_per_cu=0, gc2_resident_per_cu=2),
+            dict(gc2_unroll=2, gc2_nt=10, gc2_blocks_per_cu=3, gc2_resident_per_cu=0),
+            dict(gc2_unroll=1, gc2_nt=7, gc2_blocks_per_cu=0, gc2_resident_per_cu=4)]
 
 
 @pytest.fixture
@@ -347,3 +348,57 @@ def test_bucket_table_cache_over_many_lists(gpu):
     torch.cuda.synchronize()
     for i in range(len(big)):
         assert np.array_equal(host(o_d[i]), oracle.gc2_quantize(gs[i], np.zeros(big[i], np.float32), t))
+
+
+def test_bucket_table_eviction_waits_on_the_device(gpu):
+    # Fill all 8 cached tables from stream s1 while s1 is still busy with a
+    # long queue of work, then make a ninth distinct list on stream s2 evict
+    # a table whose kernel on s1 has not run yet.  The overwrite must wait
+    # for that kernel on the device (every result matches the oracle), and
+    # the host must not wait for it: the calls return while s1 is busy.
+    import torch
+
+    say("gc2 table eviction while its reader is queued on another stream")
+    rs = np.random.default_rng(33)
+    t = 0.03
+    big = 1 << 29
+    gb = torch.empty(big, device="cuda").normal_(0, 0.01)
+    rb = torch.zeros(big, device="cuda")
+    ob = torch.empty(big // 16, dtype=torch.int32, device="cuda")
+    lists, state = [], []
+    for k in range(9):
+        sizes = [int(x) for x in rs.integers(100, 5000, 2 + k % 2)]
+        gs = [(rs.standard_normal(n) * 0.03).astype(np.float32) for n in sizes]
+        g_d = [dev(a) for a in gs]
+        r_d = [torch.zeros(n, device="cuda") for n in sizes]
+        o_d = [torch.empty(oracle.packed_words(n), dtype=torch.int32, device="cuda")
+               for n in sizes]
+        lists.append((gpu.BucketList([(g_d[i], r_d[i], o_d[i], t) for i in range(len(sizes))]),
+                      r_d, o_d))
+        state.append((gs, [np.zeros(n, np.float32) for n in sizes]))
+    # evict whatever the cache holds from earlier tests: 8 fresh lists
+    # (one per slot) on the default stream, completed
+    for k in range(8):
+        gpu.gc2_quantize_buckets(lists[k][0])
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        for _ in range(12):                       # ~25 ms of queued work
+            gpu.gc2_quantize(gb, rb, t, out=ob)
+        for k in range(8):                        # the 8 tables, read after it
+            gpu.gc2_quantize_buckets(lists[k][0])
+    with torch.cuda.stream(s2):
+        gpu.gc2_quantize_buckets(lists[8][0])     # evicts list 0's table
+    busy = not s1.query()
+    torch.cuda.synchronize()
+    assert busy, "the host waited for stream s1"
+    for k in range(9):
+        gs, r_h = state[k]
+        steps = 2 if k < 8 else 1                 # lists 0..7 ran twice, list 8 once
+        for _ in range(steps):
+            want = [oracle.gc2_quantize(gs[i], r_h[i], t) for i in range(len(gs))]
+        _, r_d, o_d = lists[k]
+        for i in range(len(gs)):
+            assert np.array_equal(host(o_d[i]), want[i]), (k, i)
+            assert np.array_equal(bits(host(r_d[i])), bits(r_h[i])), (k, i)
+    del gb, rb, ob
