@@ -17,6 +17,7 @@ import os
 
 __all__ = [
     "GcqError", "load", "lib_path", "gc2_quantize", "gc2_quantize_buckets",
+    "gc2_quantize_buckets_noalloc", "GC2_NOALLOC_MAX_BUCKETS",
     "gc2_dequant_reduce", "qsgd_quantize", "qsgd_dequant", "gc2_packed_words",
     "qsgd_num_buckets", "qsgd_nibble_words", "MAX_WORKERS", "set_tuning", "get_tuning", "BucketList",
     "cdsgd_update_quantize", "cdsgd_local_update", "cdsgd_compresses",
@@ -78,6 +79,8 @@ def load():
     lib.gc2_quantize.restype = i32
     lib.gc2_quantize_buckets.argtypes = [ctypes.POINTER(Gc2Bucket), u32, vp]
     lib.gc2_quantize_buckets.restype = i32
+    lib.gc2_quantize_buckets_noalloc.argtypes = [ctypes.POINTER(Gc2Bucket), u32, vp]
+    lib.gc2_quantize_buckets_noalloc.restype = i32
     lib.gc2_dequant_reduce.argtypes = [ctypes.POINTER(vp), u32, sz, f32, vp, vp]
     lib.gc2_dequant_reduce.restype = i32
     lib.gcq_probe_reduce.argtypes = [ctypes.POINTER(vp), u32, sz, vp, vp]
@@ -281,6 +284,20 @@ def gc2_quantize_buckets(buckets):
     bl = buckets if isinstance(buckets, BucketList) else BucketList(buckets)
     _check(lib.gc2_quantize_buckets(bl.array, bl.count, _stream(bl.device)),
            "gc2_quantize_buckets")
+
+
+def gc2_quantize_buckets_noalloc(buckets):
+    """gc2_quantize_buckets through the entry point that allocates nothing
+    (its descriptor table is a fixed device array of the library, at most
+    GC2_NOALLOC_MAX_BUCKETS buckets; calls that may overlap on one device
+    race on it)."""
+    lib = load()
+    bl = buckets if isinstance(buckets, BucketList) else BucketList(buckets)
+    _check(lib.gc2_quantize_buckets_noalloc(bl.array, bl.count, _stream(bl.device)),
+           "gc2_quantize_buckets_noalloc")
+
+
+GC2_NOALLOC_MAX_BUCKETS = 4096
 
 
 def gc2_dequant_reduce(words, n: int, t: float, acc=None):

@@ -154,6 +154,34 @@ int ensure_capacity(Slot &s, size_t nb)
     return GCQ_OK;
 }
 
+// The device table of gc2_quantize_buckets_noalloc: a fixed array of the
+// library, one copy per device, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (in host code the name stands
+// for a host-side shadow, not the device copy); it uses the device address
+// hipGetSymbolAddress returns for the current device, kept per device.
+static_assert(sizeof(Gc2Desc) == 48, "the header states 48 bytes per descriptor");
+static __device__ __align__(256) Gc2Desc scratch[GC2_NOALLOC_MAX_BUCKETS];
+
+std::mutex g_scratch_mu;
+Gc2Desc *g_scratch_ptr[kMaxDevices];
+// Host-side working arrays of the no-alloc call (so it allocates no host
+// memory either), used under g_scratch_mu.
+Range g_na_ranges[3 * GC2_NOALLOC_MAX_BUCKETS];
+Gc2Desc g_na_descs[GC2_NOALLOC_MAX_BUCKETS];
+
+// The current device's copy of `scratch` (looked up once per device).
+int scratch_table(int dev, Gc2Desc **out)
+{
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return GCQ_ERR_LAUNCH;
+        g_scratch_ptr[dev] = (Gc2Desc *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GCQ_OK;
+}
+
 // Checks every bucket of a fused call and builds its device descriptors:
 // ranges receives up to 3 per bucket, descs one per bucket.  tpb is the
 // tile count shared by every bucket (0 if they differ): the kernel then
@@ -313,6 +341,36 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         return GCQ_ERR_LAUNCH;
     s.pending = true;
     return GCQ_OK;
+}
+
+int gc2_quantize_buckets_noalloc(const gc2_bucket *buckets, uint32_t num_buckets, void *stream)
+{
+    if (num_buckets == 0)
+        return GCQ_OK;
+    if (!buckets)
+        return GCQ_ERR_NULL;
+    if (num_buckets > GC2_NOALLOC_MAX_BUCKETS)
+        return GCQ_ERR_PARAM;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    const gcq_tuning tu = gcq::tuning();
+    RangeArray ra{g_na_ranges, 0};
+    uint64_t total_tiles = 0, tpb = 0;
+    int st = prepare_buckets(buckets, num_buckets, tu, &ra, g_na_descs, &total_tiles, &tpb);
+    if (st != GCQ_OK || total_tiles == 0)
+        return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GCQ_ERR_LAUNCH;
+    Gc2Desc *table = nullptr;
+    st = scratch_table(dev, &table);
+    if (st != GCQ_OK)
+        return st;
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = gcq::launch_gc2_table_fill(g_na_descs, num_buckets, table, hs);
+    if (e != hipSuccess)
+        return launch_status(e);
+    return launch_status(
+        gcq::launch_gc2_table(tu, table, num_buckets, total_tiles, (uint32_t)tpb, hs));
 }
 
 int cdsgd_update_quantize(const float *g, float *r, float *w_loc, size_t n, float t, float eta,

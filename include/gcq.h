@@ -141,6 +141,25 @@ typedef struct gc2_bucket {
 int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *stream);
 
 /*
+ * gc2_quantize_buckets_noalloc -- gc2_quantize_buckets for callers that
+ * cannot allocate memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks and results.  It
+ * calls no hipMalloc or hipFree and allocates no host memory: the
+ * descriptor table lives in a fixed device array of the library (room for
+ * GC2_NOALLOC_MAX_BUCKETS descriptors, 48 bytes each, 192 KiB per device,
+ * held until the process ends), which every call rewrites with small
+ * kernels on `stream` before the quantizer reads it.  Calls on one device
+ * therefore share that array: calls ordered on one stream are safe, but two
+ * calls that may run at the same time on one device (on different streams
+ * without an ordering between them) race on it and must not be made.
+ *
+ * Errors: as gc2_quantize_buckets, and GCQ_ERR_PARAM when num_buckets
+ * exceeds GC2_NOALLOC_MAX_BUCKETS.
+ */
+#define GC2_NOALLOC_MAX_BUCKETS 4096
+int gc2_quantize_buckets_noalloc(const gc2_bucket *buckets, uint32_t num_buckets, void *stream);
+
+/*
  * gc2_dequant_reduce -- the receiving side of the MXNet PR's "Local
  * kvstore" (device 0 dequantizes every device's packed gradient and sums
  * them) and "Dist kvstore" (the server dequantizes to full size).  With

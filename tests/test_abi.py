@@ -102,6 +102,29 @@ def test_gc2_buckets_validation(lib):
     assert call([(0, 0, 0, 0, 0.5), (0, 0, 0, 0, 0.5)]) == OK
 
 
+def test_gc2_buckets_noalloc_validation(lib):
+    # the entry point that allocates nothing checks exactly what
+    # gc2_quantize_buckets checks, plus its table size, all before any
+    # device call
+    def call(descs):
+        arr = (gcq.Gc2Bucket * len(descs))(*[gcq.Gc2Bucket(*d) for d in descs])
+        return lib.gc2_quantize_buckets_noalloc(arr, len(descs), NULL)
+
+    mb = 1 << 20
+    good = lambda i, n=1000: (A + 3 * i * mb, A + (3 * i + 1) * mb, A + (3 * i + 2) * mb, n, 0.5)
+    assert "#define GC2_NOALLOC_MAX_BUCKETS 4096" in open(HEADER).read()
+    assert lib.gc2_quantize_buckets_noalloc(None, 0, NULL) == OK
+    assert lib.gc2_quantize_buckets_noalloc(None, 3, NULL) == E_NULL
+    assert call([good(0), (A + 3 * mb, A + 4 * mb, A + 5 * mb, 1000, 0.0)]) == E_THR
+    assert call([good(0), (A + 3 * mb + 4, A + 4 * mb, A + 5 * mb, 1000, 0.5)]) == E_ALIGN
+    assert call([good(0), (A + 3 * mb, A, A + 5 * mb, 1000, 0.5)]) == E_OVERLAP
+    assert call([(A, A + mb, A + 2 * mb, 0, 0.5)] * 3) == OK
+    assert call([good(i, 16) for i in range(4097)]) == E_PARAM
+    half = (1 << 59) + 1
+    assert call([(A, A + (1 << 20), A + (2 << 20), half, 0.5),
+                 (A, A + (3 << 20), A + (4 << 20), half, 0.5)]) == E_PARAM
+
+
 def test_probe_validation(lib):
     ps = lambda a, b, c, w, n: lib.gcq_probe_stream(vp(a), vp(b), vp(c), vp(w), n, NULL)
     mb = 1 << 20
