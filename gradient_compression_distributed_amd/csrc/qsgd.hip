@@ -10,6 +10,8 @@
 // draw depends only on (seed, element index), never on the launch shape.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gcq_device.h"
 #include "gcq_internal.h"
 
@@ -106,6 +108,23 @@ __device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, uint32
 }
 
 __device__ __forceinline__ uint32_t sign_bit(float gv) { return gv < 0.0f ? 8u : 0u; }
+
+// Float4 q (0..3) of lane L of a full 1024-output wave tile at `tile`
+// (wave-uniform), elements 256q + 4L .. +3.  NT: a buffer store with the nt
+// and sc1 cache-policy bits (the lane-table decode at 2^30, d = 512: 0.74 ms
+// against 0.77 ms with nt alone, in one process); else a plain store.
+template <bool NT>
+__device__ __forceinline__ void st_tile_f4(float *tile, int q, uint32_t lane, v4f x)
+{
+    if constexpr (NT) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)tile, 0, (int)(kWaveElems * 4), dev::kBufferRsrcWord3);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rs, (int)((256u * q + 4u * lane) * 4u), 0,
+                                               dev::kCpolNt | dev::kCpolSc1);
+    } else {
+        *reinterpret_cast<v4f *>(tile + 256u * q + 4u * lane) = x;
+    }
+}
 
 // 16 bits of nibbles for four elements, first element in the top nibble:
 // nibble = sign << 3 | level, sign = [g < 0].  pack4_exact tests g < 0 per
@@ -261,36 +280,52 @@ __global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
         const bool fast = Rcp && rcp_norm_ok(norm) && finite_bucket;
         const float rs = fast ? (1.0f / norm) * sf : 0.0f;
         uint32_t h[R];
+        // The chunk loop in two copies: AllFast when every bucket the
+        // wavefront holds takes the division-free path (the common case),
+        // where the choice between the two nibble packings is known at
+        // compile time; otherwise each lane follows its own bucket and both
+        // packings are formed and selected.
+        auto chunks = [&](auto all_fast) {
+            constexpr bool AllFast = decltype(all_fast)::value;
+            const bool f = AllFast || fast;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float gq[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-            uint32_t cw[4];
-            philox_words4((base + CH * r + 4u * l) >> 2, k0, k1, cw);
-            uint32_t lv[4];
-            bool all_ok = false;
-            if (fast) {
-                float dist[4];
+            for (int r = 0; r < R; ++r) {
+                const float gq[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+                uint32_t cw[4];
+                philox_words4((base + CH * r + 4u * l) >> 2, k0, k1, cw);
+                uint32_t lv[4];
+                bool all_ok = false;
+                if (f) {
+                    float dist[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist[q]);
-                all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
-            }
-            if (!all_ok) {
-                // rare: the exact level where the shortcut cannot decide
-                // (its test redone here, so the fast path keeps nothing)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float dq = 1.0f;
-                    if (fast)
-                        (void)qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dq);
-                    if (!(dq < kSafeDist))
-                        lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s,
-                                                 (float)(cw[q] >> 8) * 0x1p-24f);
+                    for (int q = 0; q < 4; ++q)
+                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist[q]);
+                    all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
                 }
+                if (!all_ok) {
+                    // rare: the exact level where the shortcut cannot decide
+                    // (its test redone here, so the fast path keeps nothing)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float dq = 1.0f;
+                        if (f)
+                            (void)qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dq);
+                        if (!(dq < kSafeDist))
+                            lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s,
+                                                     (float)(cw[q] >> 8) * 0x1p-24f);
+                    }
+                }
+                // a fast bucket holds no NaN, so its signs may come from the bits
+                if constexpr (AllFast)
+                    h[r] = pack4(gq, lv);
+                else
+                    h[r] = f ? pack4(gq, lv) : pack4_exact(gq, lv);
             }
-            // a fast bucket holds no NaN, so its signs may come from the bits
-            h[r] = fast ? pack4(gq, lv) : pack4_exact(gq, lv);
-        }
+        };
+        if (__all(fast))
+            chunks(std::true_type{});
+        else
+            chunks(std::false_type{});
         uint32_t *out = nib + (base >> 3) + (l >> 1);
         const bool odd = (lane & 1u) != 0;
 #pragma unroll
@@ -446,14 +481,17 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_kernel(
                 o[q][j] = (nb & 8u) ? -v : v;
             }
         }
+        const uint64_t et0 = t * kWaveElems;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (e[q] + 4 <= n) {
-                v4f x;
-                x.x = o[q][0];
-                x.y = o[q][1];
-                x.z = o[q][2];
-                x.w = o[q][3];
+            v4f x;
+            x.x = o[q][0];
+            x.y = o[q][1];
+            x.z = o[q][2];
+            x.w = o[q][3];
+            if (et0 + kWaveElems <= n) {
+                st_tile_f4<NT>(out + et0, q, lane, x);
+            } else if (e[q] + 4 <= n) {
                 st<NT>(reinterpret_cast<v4f *>(out + e[q]), x);
             } else {
                 for (int j = 0; j < 4; ++j)
@@ -528,14 +566,17 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_dequant_lanes_kernel(
                 o[q][j] = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, tv));
             }
         }
+        const uint64_t et0 = t * kWaveElems;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (e[q] + 4 <= n) {
-                v4f x;
-                x.x = o[q][0];
-                x.y = o[q][1];
-                x.z = o[q][2];
-                x.w = o[q][3];
+            v4f x;
+            x.x = o[q][0];
+            x.y = o[q][1];
+            x.z = o[q][2];
+            x.w = o[q][3];
+            if (et0 + kWaveElems <= n) {
+                st_tile_f4<NT>(out + et0, q, lane, x);
+            } else if (e[q] + 4 <= n) {
                 st<NT>(reinterpret_cast<v4f *>(out + e[q]), x);
             } else {
                 for (int j = 0; j < 4; ++j)
