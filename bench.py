@@ -218,6 +218,14 @@ def main():
                    "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                    "bytes_per_element": BYTES[op]}
 
+    # the pair the target names: the quantizer plus the reduce, as one rate
+    # over both operations' algorithmic bytes
+    pair_s = (op_ms["gc2_quantize_buckets"] + op_ms["gc2_dequant_reduce"]) / 1e3
+    pair_bpe = BYTES["gc2_quantize_buckets"] + BYTES["gc2_dequant_reduce"]
+    gc2_pair = {"ms": round(pair_s * 1e3, 4), "bytes_per_element": pair_bpe,
+                "GBps": round(pair_bpe * n / pair_s / 1e9, 1),
+                "frac_of_peak": round(pair_bpe * n / pair_s / 1e9 / HBM_PEAK_GBPS, 4)}
+
     # fused launch vs 128 per-bucket launches of the same quantizer (untimed
     # by the step clock; events on the same stream)
     if not args.no_per_bucket:
@@ -374,6 +382,7 @@ def main():
         "ops": ops,
         "next_ops": next_ops,
         "step_elements_per_s": n / (ms_per_step / 1e3),
+        "gc2_quantize_plus_dequant_reduce": gc2_pair,
         "ceiling": ceiling,
         "configs": configs,
         "device": torch.cuda.get_device_name(dev),

@@ -8,7 +8,8 @@ element 2^32, the last bucket holds 37 elements), its dequant, the
 two-worker average (L2 and max-norm messages) and the Elias coding; the
 SAPS mask, gather and merge (the last mask word holds 5 bits).  Each
 test needs up to about 50 GiB of device memory and frees it before
-returning."""
+returning.  n = 2^34 + 4099 takes the uniforms' Philox counter past a
+change of its high word (QSGD and the SAPS mask, about 73 GiB)."""
 import numpy as np
 import pytest
 
@@ -236,4 +237,71 @@ def test_saps_past_2_32(gpu):
         want[keep] = (xo[keep] + (np.arange(rank0, rank0 + k) % 1024).astype(np.float32)) * np.float32(0.5)
         assert np.array_equal(bits(host(x[lo:hi])), bits(want)), lo
     del x, mask, offs, vals, peer
+    _free()
+
+
+# Past 2^34 elements the Philox counter q = i / 4 of the QSGD uniforms and
+# the SAPS mask has a non-zero high word: n = 2^34 + 4099 crosses that
+# boundary (high word 1 from element 2^34 on) and ends ragged (the last QSGD
+# bucket holds 3 elements, the last mask word 3 bits).
+N34 = (1 << 34) + 4099
+EDGE34 = 1 << 34
+
+
+def windows34(n, align):
+    out = []
+    for lo in (0, EDGE34 - 4 * align, EDGE34 - align, n - (n % align) - align):
+        lo -= lo % align
+        out.append((lo, min(n, lo + 8 * align)))
+    return out
+
+
+def test_qsgd_past_2_34(gpu):
+    """QSGD d = 512 (L2 and max-norm) for 2^34 + 4099 elements: norms,
+    nibbles at their global indices on both sides of element 2^34 and in
+    the ragged tail, against the oracle (about 73 GiB of device memory)."""
+    import torch
+
+    say("qsgd n", N34)
+    d, s, seed = 512, 7, 0x5EED34
+    g = torch.empty(N34, device="cuda").normal_(0.0, 0.01, generator=torch.Generator("cuda").manual_seed(16))
+    for maxnorm in (False, True):
+        norms, nib = gpu.qsgd_quantize(g, d, s, seed, maxnorm=maxnorm)
+        torch.cuda.synchronize()
+        for lo, hi in windows34(N34, d):
+            gh = host(g[lo:hi])
+            got = host(norms[lo // d:(hi + d - 1) // d])
+            if maxnorm:
+                assert np.array_equal(bits(got), bits(oracle.qsgd_maxnorms(gh, d))), lo
+            else:
+                np.testing.assert_allclose(got, oracle.qsgd_norms(gh, d), rtol=1e-6)
+            want = oracle.qsgd_levels(gh, d, s, seed, got, index_base=lo)
+            assert np.array_equal(host(nib[lo // 8:(hi + 7) // 8]), want), (maxnorm, lo)
+        del norms, nib
+        _free()
+    del g
+    _free()
+
+
+def test_saps_mask_past_2_34(gpu):
+    """The SAPS mask for 2^34 + 4099 elements: mask bits on both sides of
+    element 2^34 and in the 3-bit last word against the oracle's keep rule,
+    the tile offsets there, and the total against the mask's popcount."""
+    import torch
+
+    say("saps mask n", N34)
+    c, seed = 100.0, 0x5A9534
+    mask, offs = gpu.saps_mask(N34, c, seed)
+    total = gpu.saps_count(offs)
+    mask_h = host(mask)
+    assert mask_h.size == (N34 + 31) // 32
+    assert total == _popcount(mask_h)
+    offs_h = host(offs).view(np.int64)
+    for lo, hi in ((EDGE34 - 16384, N34 - 3), (N34 - 4099, N34)):
+        keep = oracle.saps_keep(seed, hi - lo, c, start=lo)
+        got = (mask_h[np.arange(lo, hi) // 32] >> (np.arange(lo, hi) % 32).astype(np.uint32)) & 1
+        assert np.array_equal(got.astype(bool), keep), lo
+        t0 = lo // 8192                 # lo is a multiple of 8192: offs[t0] = kept before lo
+        assert offs_h[t0] == _popcount(mask_h[:lo // 32]), lo
+    del mask, offs
     _free()
