@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "gcq.h"
@@ -278,8 +279,16 @@ int gc2_quantize_buckets(const gc2_bucket *buckets, uint32_t num_buckets, void *
         return GCQ_ERR_NULL;
     if (num_buckets > 0x7FFFFFFFu)
         return GCQ_ERR_PARAM;
-    std::vector<Range> ranges(3 * (size_t)num_buckets);
-    std::vector<Gc2Desc> descs(num_buckets);
+    // host working arrays sized by the caller's count: a failed allocation
+    // is reported, never thrown across the C boundary
+    std::vector<Range> ranges;
+    std::vector<Gc2Desc> descs;
+    try {
+        ranges.resize(3 * (size_t)num_buckets);
+        descs.resize(num_buckets);
+    } catch (const std::bad_alloc &) {
+        return GCQ_ERR_NOMEM;
+    }
     const gcq_tuning tu = gcq::tuning();
     RangeArray ra{ranges.data(), 0};
     uint64_t total_tiles = 0, tpb = 0;
