@@ -48,7 +48,7 @@ class Tuning(ctypes.Structure):
         "dq_lds_stores", "dq_blocks_per_cu", "dq_fp4_decode", "qsgd_nt", "qsgd_rcp",
         "qsgd_dequant_nt", "qsgd_blocks_per_cu", "qsgd_dequant_blocks_per_cu",
         "qsgd_buckets_per_wave", "dq_words_per_thread", "dq_resident_per_cu",
-        "gc2_resident_per_cu")]
+        "gc2_resident_per_cu", "cdsgd_resident_per_cu", "qsgd_avg_resident_per_cu")]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -399,7 +399,7 @@ hipError_t launch_cdsgd(const float *g, float *r, float *w, uint32_t *out, uint6
         return hipSuccess;
     const Gc2Desc one = {g, r, out, n, 0, t, 0};
     const uint32_t grid = grid_for(tiles, tu.gc2_blocks_per_cu);
-    const uint32_t pad = resident_lds_pad(0, tu.gc2_resident_per_cu);
+    const uint32_t pad = resident_lds_pad(0, tu.cdsgd_resident_per_cu);
     switch (tu.gc2_unroll) {
     case 1: launch_cdsgd_nt<1>(tu.gc2_nt, quant, grid, pad, one, w, eta, tiles, stream); break;
     case 2: launch_cdsgd_nt<2>(tu.gc2_nt, quant, grid, pad, one, w, eta, tiles, stream); break;

@@ -63,6 +63,12 @@ void init_locked()
     g_tuning.gc2_resident_per_cu = env_int("GCQ_GC2_RESIDENT_PER_CU", 0);
     if (!resident_ok(g_tuning.gc2_resident_per_cu))
         g_tuning.gc2_resident_per_cu = 0;
+    g_tuning.cdsgd_resident_per_cu = env_int("GCQ_CDSGD_RESIDENT_PER_CU", 5);
+    if (!resident_ok(g_tuning.cdsgd_resident_per_cu))
+        g_tuning.cdsgd_resident_per_cu = 5;
+    g_tuning.qsgd_avg_resident_per_cu = env_int("GCQ_QSGD_AVG_RESIDENT_PER_CU", 0);
+    if (!resident_ok(g_tuning.qsgd_avg_resident_per_cu))
+        g_tuning.qsgd_avg_resident_per_cu = 0;
     g_init = true;
 }
 
@@ -88,7 +94,8 @@ bool tuning_valid(const gcq_tuning &t)
            (t.qsgd_buckets_per_wave == 0 || t.qsgd_buckets_per_wave == 1 ||
             t.qsgd_buckets_per_wave == 2 || t.qsgd_buckets_per_wave == 4) &&
            (t.dq_words_per_thread == 1 || t.dq_words_per_thread == 2) &&
-           resident_ok(t.dq_resident_per_cu) && resident_ok(t.gc2_resident_per_cu);
+           resident_ok(t.dq_resident_per_cu) && resident_ok(t.gc2_resident_per_cu) &&
+           resident_ok(t.cdsgd_resident_per_cu) && resident_ok(t.qsgd_avg_resident_per_cu);
 }
 
 void set_tuning(const gcq_tuning &t)
@@ -116,12 +123,33 @@ int device_cus()
     return cache[dev];
 }
 
+// Largest LDS allocation of one workgroup on the current device (cached).
+uint32_t device_max_lds()
+{
+    static std::mutex mu;
+    static uint32_t cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 64u * 1024u;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 64 * 1024;
+        cache[dev] = (uint32_t)v;
+    }
+    return cache[dev];
+}
+
 uint32_t resident_lds_pad(uint32_t static_bytes, int resident)
 {
     if (resident <= 0)
         return 0;
     const uint32_t per = dev::kLdsBytesPerCu / (uint32_t)resident - 1024u;
-    return per > static_bytes ? per - static_bytes : 0u;
+    const uint32_t cap = device_max_lds();
+    const uint32_t want = per < cap ? per : cap;
+    return want > static_bytes ? want - static_bytes : 0u;
 }
 
 uint32_t grid_for(uint64_t work_blocks, int blocks_per_cu)

@@ -996,8 +996,9 @@ hipError_t launch_qsgd_average(const QsgdMsgs &ms, uint32_t K, uint64_t n, uint3
         const uint32_t grid = grid_for(ntiles, tu.qsgd_dequant_blocks_per_cu);
         // a nibble word never straddles a bucket boundary when 8 divides d
         const bool uni = (d & 7u) == 0u;
+        const uint64_t lds_run = lds + resident_lds_pad((uint32_t)lds, tu.qsgd_avg_resident_per_cu);
 #define GCQ_AVG(P, NT, U)                                                                     \
-    qsgd_average_kernel<P, NT, U><<<grid, kBlockThreads, (size_t)lds, stream>>>(              \
+    qsgd_average_kernel<P, NT, U><<<grid, kBlockThreads, (size_t)lds_run, stream>>>(          \
         ms, K, n, d, s, kf, ntiles, out)
 #define GCQ_AVG_U(P, NT)                                                                      \
     do {                                                                                      \

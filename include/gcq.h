@@ -533,8 +533,13 @@ typedef struct gcq_tuning {
                                workgroups resident per compute unit, set through
                                the kernel's LDS allocation: 0 (no cap) or 2..8
                                (default 3) */
-    int gc2_resident_per_cu; /* the 2-bit quantizer and the CD-SGD kernels:
-                               the same cap, 0 (no cap, default) or 2..8 */
+    int gc2_resident_per_cu; /* the 2-bit quantizer: the same cap, 0 (no cap,
+                               default) or 2..8 */
+    int cdsgd_resident_per_cu; /* the CD-SGD kernels (update fused with the
+                               quantizer, update alone): the same cap, 0 (no
+                               cap) or 2..8 (default 5) */
+    int qsgd_avg_resident_per_cu; /* qsgd_dequant_average: the same cap, 0
+                               (no cap, default) or 2..8 */
 } gcq_tuning;
 
 /*
@@ -543,7 +548,8 @@ typedef struct gcq_tuning {
  * variables GCQ_GC2_UNROLL, GCQ_GC2_NT, GCQ_GC2_BLOCKS_PER_CU,
  * GCQ_DQ_NT_LOADS, GCQ_DQ_NT_STORES, GCQ_DQ_LDS_STORES, GCQ_DQ_FP4_DECODE,
  * GCQ_DQ_BLOCKS_PER_CU, GCQ_DQ_WORDS_PER_THREAD, GCQ_DQ_RESIDENT_PER_CU,
- * GCQ_GC2_RESIDENT_PER_CU, GCQ_QSGD_NT, GCQ_QSGD_RCP,
+ * GCQ_GC2_RESIDENT_PER_CU, GCQ_CDSGD_RESIDENT_PER_CU, GCQ_QSGD_AVG_RESIDENT_PER_CU,
+ * GCQ_QSGD_NT, GCQ_QSGD_RCP,
  * GCQ_QSGD_DEQUANT_NT, GCQ_QSGD_BLOCKS_PER_CU, GCQ_QSGD_DEQUANT_BLOCKS_PER_CU
  * and GCQ_QSGD_BUCKETS_PER_WAVE when set (block counts and gc2_nt are
  * clamped into range, a flag reads any nonzero value as 1, and any other
@@ -555,8 +561,8 @@ typedef struct gcq_tuning {
  * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
  * flag not 0/1, gc2_nt outside 0..15, gc2_unroll not 1/2/4, a block
  * count outside 0..1024, qsgd_buckets_per_wave not 0/1/2/4,
- * dq_words_per_thread not 1/2, dq_resident_per_cu or gc2_resident_per_cu
- * not 0 or 2..8); on error
+ * dq_words_per_thread not 1/2, a *_resident_per_cu knob not 0 or 2..8); on
+ * error
  * nothing changes.
  */
 int gcq_get_tuning(gcq_tuning *out);

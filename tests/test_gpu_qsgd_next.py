@@ -130,8 +130,9 @@ def check_average(gpu, scales, nibs, n, d, s):
 def test_average_workers(knobs, K):
     gpu = knobs
     say("qsgd average K", K)
-    for dbpc, nt in ((0, 1), (3, 0)):
-        gpu.set_tuning(qsgd_dequant_blocks_per_cu=dbpc, qsgd_dequant_nt=nt)
+    for dbpc, nt, cap in ((0, 1, 0), (3, 0, 2), (0, 1, 5)):
+        gpu.set_tuning(qsgd_dequant_blocks_per_cu=dbpc, qsgd_dequant_nt=nt,
+                       qsgd_avg_resident_per_cu=cap)
         for n, d in ((2048, 512), (2049, 512), (100_003, 512), (65_536 + 17, 256), (10_000, 1000),
                      (50_000, 4096), (9_000, 64), (777, 1), (20_000, 255), (30_000, 341),
                      (30_000, 340)):
