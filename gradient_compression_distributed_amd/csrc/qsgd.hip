@@ -72,39 +72,71 @@ __device__ __forceinline__ uint32_t qsgd_level_exact(float gabs, float norm, flo
 // (u in [0, 1); the integer case x - u = l is p = u, level l).  With
 // T = x + 1 - u > 0 that is trunc(T) whenever T is not an integer.  The
 // clamp needs no case of its own: |g| <= norm for the L2 norm (the float64
-// sum of squares and its square root only round towards values >= g^2 and
-// |g|) and for the largest magnitude, so a = RN(|g|/norm) <= 1 and x <= s;
-// x = s gives T in (s, s + 1], whose trunc is s unless T = s + 1 (u = 0),
-// an integer.
+// sum of exact squares only rounds towards values >= g^2, and bucket_norm's
+// square root is within 2^-40 of exact before its rounding to float, which
+// cannot fall below the float |g|) and for the largest magnitude, so
+// a = RN(|g|/norm) <= 1 and x <= s; x = s gives T in (s, s + 1], whose trunc
+// is s unless T = s + 1 (u = 0), an integer.
 //
-// The kernel computes d1 = RN(t - U' 2^-32) with t = RN(|g| rs + 1) (one
-// fma), rs = RN(RN(1/norm) s), and U' = RN(c) the raw 32-bit Philox word
-// converted to float (no shift).  For a bucket norm in [2^-120, 2^120]:
-//   |g| rs is within 4 relative roundings of x (two on each side, on a value
-//     below 7.0001): 28 * 2^-24;
-//   t rounds |g| rs + 1 < 9 once: at most 2^-21 = 8 * 2^-24;
+// The kernel computes d = RN(t - U' 2^-32) with t = RN(|g| rs + 1 + kGuard)
+// (one fma), rs = RN(r s) for r the reciprocal of the norm from
+// recip_refined (within one ulp of 1/norm, in fact within one rounding and
+// 2^-45), and U' = RN(c) the raw 32-bit Philox word converted to float (no
+// shift).  For a bucket norm in [2^-120, 2^120]:
+//   |g| rs is within 5 relative half-ulps of x (two roundings in x, the
+//     ulp of r and the rounding of rs, on a value below 7.0001):
+//     35.1 * 2^-24;
+//   t rounds |g| rs + 1 + kGuard < 9 once: at most 2^-21 = 8 * 2^-24;
 //   U' 2^-32 is within 2^-24 (the 8 dropped bits) + 2^-25 (the conversion)
 //     of u = (c >> 8) 2^-24: 1.5 * 2^-24;
 //   the fma rounds t - U' 2^-32 < 9 once: 8 * 2^-24;
-// so |d1 - T| < 46 * 2^-24 < kGuard = 2^-18.  Whenever d1 lies more than
-// kGuard from every integer, trunc(d1) = trunc(T), the exact level (and d1
-// then stays below s + 1 - kGuard, so the level fits its 3 bits).  The
-// shortcut only runs for finite buckets (a NaN or Inf element makes the
-// norm NaN or Inf, outside the range), so d1 is finite and d1 >= 0.
+// so |d - (T + kGuard)| < 53 * 2^-24 < kGuard = 2^-18.  When fract(d) >= 2
+// kGuard, T lies strictly between trunc(d) and trunc(d) + 1: trunc(d) =
+// trunc(T), the exact level (T <= s + 1 then keeps it at most s, within its
+// 3 bits).  The shortcut only runs for finite buckets (a NaN or Inf element
+// makes the norm NaN or Inf, outside the range), so d is finite and d > 0.
 constexpr float kGuard = 0x1p-18f;
-// kGuard < f < 1 - kGuard for f = fract(d1) (exact for d1 in [0, 9)), as
-// one comparison of |f - 0.5|; its rounding is monotone and 0.5 - kGuard is
-// a float, so it only ever errs towards "unsafe".
-constexpr float kSafeDist = 0.5f - kGuard;
+// fract(d) is exact for d in [0, 9); one comparison per element group.
+constexpr float kSafeFrac = 2.0f * kGuard;
 
-// Level from the shortcut; `dist` = |fract(d1) - 0.5|, safe when below
-// kSafeDist (an unsafe lane's return value is not used).
-__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, uint32_t c, float &dist)
+// Level from the shortcut; `frac` = fract(d), safe when >= kSafeFrac (an
+// unsafe lane's return value is not used).
+__device__ __forceinline__ uint32_t qsgd_level_fast(float gabs, float rs, uint32_t c, float &frac)
 {
-    const float t = __builtin_fmaf(gabs, rs, 1.0f);
-    const float d1 = __builtin_fmaf((float)c, -0x1p-32f, t);
-    dist = __builtin_fabsf(__builtin_amdgcn_fractf(d1) - 0.5f);
-    return (uint32_t)d1;                     // d1 in [0, s + 2): in range
+    const float t = __builtin_fmaf(gabs, rs, 1.0f + kGuard);
+    const float d = __builtin_fmaf((float)c, -0x1p-32f, t);
+    frac = __builtin_amdgcn_fractf(d);
+    return (uint32_t)d;                      // d in (0, s + 2): in range
+}
+
+// 1/x for x in [2^-120, 2^120]: the hardware reciprocal (documented within
+// one ulp) and one Newton step, r (2 - x r), rounded once: the unrounded
+// step is within e^2 (plus 2^-47 from rounding 1 - x r) of 1/x for an
+// estimate within e, so the result is within one rounding and 2^-45 of 1/x.
+__device__ __forceinline__ float recip_refined(float x)
+{
+    const float r0 = __builtin_amdgcn_rcpf(x);
+    const float e = __builtin_fmaf(-x, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+
+// A bucket's L2 norm from its float64 sum of squares ss (every partial sum
+// of exact squares of floats, so 0 or in [2^-298, 2^266]): RN32(sqrt(ss)).
+// The hardware reciprocal square root y (an estimate within b of 1/sqrt(ss))
+// and h = ss y, then two corrections h += (ss - h^2) y / 2, each of which
+// takes a relative error a to about -(a b + a^2 / 2): from b to within 1.5
+// b^3 + 2^-52, below 2^-40 for any b <= 2^-13.  The float rounding then
+// equals the correctly rounded one except within 2^-40 of a halfway point,
+// and never undershoots the float |g| of any element.  ss = 0, Inf or NaN
+// gives ss itself.
+__device__ __forceinline__ float bucket_norm(double ss)
+{
+    const double y = __builtin_amdgcn_rsq(ss);
+    const double hy = 0.5 * y;
+    double h = ss * y;
+    h = __builtin_fma(__builtin_fma(-h, h, ss), hy, h);
+    h = __builtin_fma(__builtin_fma(-h, h, ss), hy, h);
+    return ss > 0.0 && ss < __builtin_inf() ? (float)h : (float)ss;
 }
 
 __device__ __forceinline__ uint32_t sign_bit(float gv) { return gv < 0.0f ? 8u : 0u; }
@@ -271,14 +303,14 @@ __global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
                 ss = __builtin_fma((double)v[r].w, (double)v[r].w, ss);
             }
             ss = group_sum<G>(ss);
-            norm = (float)__builtin_sqrt(ss);
+            norm = bucket_norm(ss);
         }
         if constexpr (H == 1)
             norm = uniform_f(norm);   // wave-uniform: scalar registers from here on
         if (own && l == 0)
             norms[b] = norm;
         const bool fast = Rcp && rcp_norm_ok(norm) && finite_bucket;
-        const float rs = fast ? (1.0f / norm) * sf : 0.0f;
+        const float rs = fast ? recip_refined(norm) * sf : 0.0f;
         uint32_t h[R];
         // The chunk loop in two copies: AllFast when every bucket the
         // wavefront holds takes the division-free path (the common case),
@@ -296,23 +328,23 @@ __global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
                 uint32_t lv[4];
                 bool all_ok = false;
                 if (f) {
-                    float dist[4];
+                    float fr[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        lv[q] = qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dist[q]);
-                    all_ok = fmaxf(fmaxf(dist[0], dist[1]), fmaxf(dist[2], dist[3])) < kSafeDist;
+                    for (int e = 0; e < 4; ++e)
+                        lv[e] = qsgd_level_fast(fabsf(gq[e]), rs, cw[e], fr[e]);
+                    all_ok = fminf(fminf(fr[0], fr[1]), fminf(fr[2], fr[3])) >= kSafeFrac;
                 }
                 if (!all_ok) {
                     // rare: the exact level where the shortcut cannot decide
                     // (its test redone here, so the fast path keeps nothing)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float dq = 1.0f;
+                    for (int e = 0; e < 4; ++e) {
+                        float fe = 0.0f;
                         if (f)
-                            (void)qsgd_level_fast(fabsf(gq[q]), rs, cw[q], dq);
-                        if (!(dq < kSafeDist))
-                            lv[q] = qsgd_level_exact(fabsf(gq[q]), norm, sf, s,
-                                                     (float)(cw[q] >> 8) * 0x1p-24f);
+                            (void)qsgd_level_fast(fabsf(gq[e]), rs, cw[e], fe);
+                        if (!(fe >= kSafeFrac))
+                            lv[e] = qsgd_level_exact(fabsf(gq[e]), norm, sf, s,
+                                                     (float)(cw[e] >> 8) * 0x1p-24f);
                     }
                 }
                 // a fast bucket holds no NaN, so its signs may come from the bits
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_thread_kernel(
             double ss = 0.0;
             for (uint64_t e = lo; e < hi; ++e)
                 ss = __builtin_fma((double)g[e], (double)g[e], ss);
-            norms[b] = (float)__builtin_sqrt(ss);
+            norms[b] = bucket_norm(ss);
         }
     }
 }
@@ -397,7 +429,7 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_norms_wave_kernel(
                 ss = __builtin_fma((double)g[e], (double)g[e], ss);
             ss = group_sum<kWave>(ss);
             if (lane == 0)
-                norms[b] = (float)__builtin_sqrt(ss);
+                norms[b] = bucket_norm(ss);
         }
     }
 }

@@ -8,7 +8,8 @@
 //             quantizer's stream), keeps element i when U_i < T with
 //             T = ceil(2^24 / c) (exactly u_i c < 1), tested on the raw
 //             32-bit word as c_i <= 256 T - 1 (U_i = c_i >> 8; T is in
-//             [1, 2^24] for c in [1, inf), so 256 T - 1 fits 32 bits),
+//             [1, 2^24] for c in [1, inf), so 256 T - 1 fits 32 bits) by
+//             the carry of a 64-bit add,
 //             writes one 32-bit mask word (bit j = element 32w + j) and the
 //             tile's kept count;
 //   scan   -- the tile counts become exclusive offsets (and the total);
@@ -58,20 +59,33 @@ __global__ __launch_bounds__(kSapsThreads) void saps_mask_kernel(uint64_t n, uin
 {
     __shared__ uint32_t wsum[kSapsThreads / kWave];
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    // Element dropped when c > Tm, i.e. when c + (2^32 - 1 - Tm) carries
+    // into bit 32.  With a factor of 1 the compiler cannot see, c * one + m
+    // is one v_mad_u64_u32 whose high word is that carry, and the bit goes
+    // into place with one shift-or: two instructions per element, where a
+    // compare, a select and an or take three or more.
+    const uint64_t m = 0xFFFFFFFFull - Tm;
+    uint32_t one = 1;
+    asm volatile("" : "+s"(one));
     for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const uint64_t wi = tile * kSapsThreads + tid;
         const uint64_t e0 = wi * 32u;
         uint32_t word = 0;
         if (e0 < n) {
+            uint32_t drop = 0;
 #pragma unroll
             for (uint32_t j = 0; j < 8; ++j) {
                 const uint64_t q = (e0 >> 2) + j;
                 uint32_t c[4] = {(uint32_t)q, (uint32_t)(q >> 32), 0u, 0u};
                 philox4x32_10(c, k0, k1);
 #pragma unroll
-                for (uint32_t r = 0; r < 4; ++r)
-                    word |= (c[r] <= Tm ? 1u : 0u) << (4 * j + r);
+                for (uint32_t r = 0; r < 4; ++r) {
+                    uint32_t carry = (uint32_t)(((uint64_t)c[r] * one + m) >> 32);
+                    asm("" : "+v"(carry));   // keeps the shift-or from folding into the product
+                    drop |= carry << (4 * j + r);
+                }
             }
+            word = ~drop;
             if (n - e0 < 32u)
                 word &= (1u << (uint32_t)(n - e0)) - 1u;   // elements past n are not kept
             st<true>((GCQ_GLOBAL uint32_t *)mask + wi, word);

@@ -4,35 +4,48 @@ The level (QSGD summary, Knowl 1) is l + [u < x - l] with x = RN(RN(|g| /
 norm) * s), l = floor(x), clamped to s, and u = (c >> 8) 2^-24 for the raw
 32-bit generator word c.  With T = x + 1 - u that level is trunc(T) whenever
 T is not an integer (|g| <= norm, so x <= s).  The kernel computes
-d1 = RN(RN(|g| rs + 1) - RN(c) 2^-32), rs = RN(RN(1/norm) * s) (two fmas),
-which stays within 46 * 2^-24 < 2^-18 of T for a norm in [2^-120, 2^120],
-and takes trunc(d1) wherever fract(d1) lies more than 2^-18 from 0 and 1;
-otherwise the IEEE division.  These tests check the bound, the identity, and
-the decisions against the level's definition on random and near-tie inputs.
+d = RN(RN(|g| rs + 1 + 2^-18) - RN(c) 2^-32), rs = RN(r * s) (two fmas) for
+a reciprocal r of the norm within one ulp (hardware estimate and a Newton
+step), which stays within 53 * 2^-24 < 2^-18 of T + 2^-18 for a norm in
+[2^-120, 2^120], and takes trunc(d) wherever fract(d) >= 2^-17; otherwise
+the IEEE division.  These tests check the bound (with r rounded either way
+from 1/norm, the worst the kernel can hold), the identity, and the
+decisions against the level's definition on random and near-tie inputs.
 
 The model below evaluates each fma as an exact float64 value rounded once
-to float32.  RN(|g| rs + 1) goes through a float64 sum, which is exact for
-|g| rs >= 2^-5 and otherwise rounds twice; a double rounding that lands on
-a different float32 needs the float64 sum to fall exactly on a float32
-midpoint, which random inputs do not reach."""
+to float32.  RN(|g| rs + 1 + 2^-18) goes through a float64 sum, which is
+exact for |g| rs >= 2^-5 and otherwise rounds twice; a double rounding
+that lands on a different float32 needs the float64 sum to fall exactly on
+a float32 midpoint, which random inputs do not reach."""
 import numpy as np
 
 F = np.float32
 GUARD = 2.0 ** -18
 
 
-def _rs(norm, s):
-    return ((F(1) / norm).astype(F) * F(s)).astype(F)
+def _recip(norm, way=0):
+    """1/norm rounded to nearest (way 0), down (-1) or up (+1) in float32."""
+    r = (F(1) / norm).astype(F)
+    if way == 0:
+        return r
+    exact = 1.0 / norm.astype(np.float64)
+    below = np.where(r.astype(np.float64) > exact, np.nextafter(r, F(0)), r)
+    above = np.where(r.astype(np.float64) < exact, np.nextafter(r, F(np.inf)), r)
+    return (below if way < 0 else above).astype(F)
+
+
+def _rs(norm, s, way=0):
+    return (_recip(norm, way) * F(s)).astype(F)
 
 
 def _x_exact(g, norm, s):
     return ((np.abs(g) / norm).astype(F) * F(s)).astype(F)
 
 
-def _d1(g, norm, s, c):
-    """The kernel's d1 = RN(RN(|g| rs + 1) - RN(c) 2^-32)."""
-    P = np.abs(g).astype(np.float64) * _rs(norm, s).astype(np.float64)   # exact product
-    t = (P + 1.0).astype(F)
+def _d(g, norm, s, c, way=0):
+    """The kernel's d = RN(RN(|g| rs + 1 + 2^-18) - RN(c) 2^-32)."""
+    P = np.abs(g).astype(np.float64) * _rs(norm, s, way).astype(np.float64)   # exact product
+    t = (P + (1.0 + GUARD)).astype(F)
     up = np.asarray(c, dtype=np.uint64).astype(F).astype(np.float64) * 2.0 ** -32
     return (t.astype(np.float64) - up).astype(F)    # exact difference, one rounding
 
@@ -47,12 +60,11 @@ def _exact_levels(g, norm, s, c):
     return np.where(x >= F(s), s, lev)
 
 
-def _shortcut(g, norm, s, c):
-    d1 = _d1(g, norm, s, c)
-    f = (d1 - np.floor(d1)).astype(F)                  # v_fract: exact on [0, 9)
-    dist = np.abs((f - F(0.5)).astype(F))
-    safe = dist < F(0.5) - F(GUARD)
-    return np.trunc(d1).astype(np.int64), safe
+def _shortcut(g, norm, s, c, way=0):
+    d = _d(g, norm, s, c, way)
+    f = (d - np.floor(d)).astype(F)                    # v_fract: exact on [0, 10)
+    safe = f >= F(2 * GUARD)
+    return np.trunc(d).astype(np.int64), safe
 
 
 def _words(rs, U):
@@ -62,7 +74,7 @@ def _words(rs, U):
 
 def test_level_error_bound():
     rs = np.random.default_rng(3)
-    bound = 46.0 * 2.0 ** -24
+    bound = 53.0 * 2.0 ** -24
     assert bound < GUARD
     for s in range(1, 8):
         for norm_exp in (-120, -60, -20, 0, 20, 60, 119):
@@ -79,9 +91,10 @@ def test_level_error_bound():
             assert np.all(x <= s)
             u = (c >> np.uint64(8)).astype(np.float64) * 2.0 ** -24
             T = x + 1.0 - u                               # exact in float64
-            d1 = _d1(g, norm, s, c).astype(np.float64)
-            assert np.all(np.abs(d1 - T) < bound), (s, norm_exp)
-            assert np.all(d1 >= 0)
+            for way in (-1, 0, 1):
+                d = _d(g, norm, s, c, way).astype(np.float64)
+                assert np.all(np.abs(d - (T + GUARD)) < bound), (s, norm_exp, way)
+                assert np.all(d > 0)
 
 
 def test_trunc_identity_matches_definition():
@@ -132,9 +145,10 @@ def test_shortcut_decides_like_the_definition():
             c[1000:1100] = U[1000:1100].astype(np.uint64) << np.uint64(8)   # low byte 0
             c[1100:1200] = (U[1100:1200].astype(np.uint64) << np.uint64(8)) | np.uint64(255)
             exact = _exact_levels(g, norm, s, c)
-            lev, safe = _shortcut(g, norm, s, c)
-            assert np.array_equal(lev[safe], exact[safe]), (s, norm_exp)
-            assert np.all(lev[safe] <= s) and np.all(lev[safe] >= 0)
+            for way in (-1, 0, 1):
+                lev, safe = _shortcut(g, norm, s, c, way)
+                assert np.array_equal(lev[safe], exact[safe]), (s, norm_exp, way)
+                assert np.all(lev[safe] <= s) and np.all(lev[safe] >= 0)
             total_unsafe += int((~safe).sum())
             total += m
     # the fallback is for near-ties only (here heavily over-sampled)
@@ -162,6 +176,6 @@ def test_planted_mistakes_fail():
     g = np.minimum(np.abs(g), norm) * np.sign(g)
     c = rs.integers(0, 1 << 32, g.size, dtype=np.uint64)
     exact = _exact_levels(g, norm, 7, c)
-    d1 = _d1(g, norm, 7, c)
-    wrong = np.trunc(d1 - F(1)).astype(np.int64)       # no +1: trunc(x - u)
+    d = _d(g, norm, 7, c)
+    wrong = np.trunc(d - F(1)).astype(np.int64)        # no +1: trunc(x - u)
     assert not np.array_equal(wrong, exact)
