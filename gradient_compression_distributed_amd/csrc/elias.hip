@@ -19,16 +19,17 @@
 //              into the offsets array, then an exclusive scan;
 //   zero    -- each bucket that starts inside a word clears that word (it is
 //              shared with the previous bucket);
-//   write   -- the non-zero coordinates of a step are compacted into an LDS
-//              list (a wavefront scan of the lanes' counts), then coded 64 at
-//              a time, one per lane, at positions from a second scan; codes
-//              are ORed into the bucket's bits in LDS, which leave as plain
-//              stores (atomic ORs for the two words a bucket may share).
+//   write   -- each lane codes the coordinates of its nibble word, one per
+//              pass of a per-lane loop, at the bit position a wavefront scan
+//              of the lanes' code lengths gives it; codes are ORed into the
+//              bucket's bits in LDS, which leave as plain stores (atomic ORs
+//              for the two words a bucket may share).
 // Decode: one lane per bucket (variable-length codes are read in order), a
 // wavefront per 64 consecutive buckets.  Their bits, one contiguous range,
 // are first copied into LDS with coalesced loads; each coordinate is then
-// parsed from a 64-bit register window.  Every read stays inside the
-// bucket and the input.
+// parsed from a 64-bit register window and ORed into the lane's nibble
+// chunk in LDS, which leaves as one 16-byte store per 32 coordinates.
+// Every read stays inside the bucket and the input.
 #include "gcq_device.h"
 #include "gcq_internal.h"
 
@@ -451,7 +452,11 @@ __device__ __forceinline__ uint32_t coord_peek(uint32_t x, uint32_t &dist, uint3
     return dlen && slen ? dlen + slen : 0u;
 }
 
-constexpr uint32_t kDecodeStageWords = 2048;   // per wavefront
+// Staged input words per wavefront: 31 per lane, so that with the decode
+// tables and the nibble chunks (40,064 bytes a workgroup) four workgroups fit
+// a compute unit's 160 KiB of LDS.
+constexpr uint32_t kDecodeStageWords = 31u * kWave;
+static_assert(kDecodeStageWords % kWave == 0, "the staging copy moves whole wavefront rows");
 
 // Decode tables for the common short codes (built per workgroup):
 //   distance table, indexed by the window's next 11 bits: (length << 8) |
@@ -477,24 +482,33 @@ __device__ __forceinline__ uint32_t level_entry(uint32_t j)
     return slen && slen <= kLevelBits && level <= 7u ? (slen << 4) | (sign << 3) | level : 0u;
 }
 
+// The nibble words being built, CW per thread, in LDS: word k of thread t
+// at lds[k * kBlockThreads + t], so the lanes of a wavefront touch
+// consecutive banks.  Each thread owns its words (no barrier needed); a
+// coordinate is ORed in with one LDS atomic, no register state to select
+// among or carry through the loop.
 template <uint32_t CW>
-struct NibChunk {
-    uint32_t c[CW];
-    __device__ void clear()
+struct LdsChunk {
+    uint32_t *own;   // word 0 of this thread
+    __device__ void clear() const
     {
 #pragma unroll
         for (uint32_t k = 0; k < CW; ++k)
-            c[k] = 0u;
+            own[k * kBlockThreads] = 0u;
     }
-    __device__ void put(uint32_t q, uint32_t v)   // word q of the chunk |= v
+    __device__ void put(uint32_t k, uint32_t v) const   // word k of the chunk |= v
     {
-#pragma unroll
-        for (uint32_t k = 0; k < CW; ++k)
-            c[k] |= q == k ? v : 0u;
+        __hip_atomic_fetch_or(own + k * kBlockThreads, v, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    // chunk ch of the bucket's nw words
+    // chunk ch of the bucket's nw words, from LDS (or zeros)
+    template <bool Zero>
     __device__ void store(uint32_t *__restrict__ nib, uint32_t ch, uint32_t nw) const
     {
+        uint32_t c[CW];
+#pragma unroll
+        for (uint32_t k = 0; k < CW; ++k)
+            c[k] = Zero ? 0u : own[k * kBlockThreads];
         if constexpr (CW == 4) {
             if (ch * 4u + 4u <= nw) {
                 uint4 v;
@@ -517,7 +531,8 @@ template <uint32_t CW, typename Src>
 __device__ __forceinline__ void decode_bucket(Src src, uint64_t start, uint64_t end, uint32_t blen,
                                               bool valid, float *norm_out,
                                               uint32_t *__restrict__ nib,
-                                              const uint16_t *dist_tab, const uint8_t *level_tab)
+                                              const uint16_t *dist_tab, const uint8_t *level_tab,
+                                              LdsChunk<CW> chunk)
 {
     const uint64_t span = valid ? end - start : 0u;
     BitReader<Src> r{src, 0u, span < (1ull << 31) ? (uint32_t)span : (1u << 31), 0u, 0u, valid};
@@ -536,15 +551,17 @@ __device__ __forceinline__ void decode_bucket(Src src, uint64_t start, uint64_t 
         *norm_out = norm;
     bool active = r.ok && r.left;
     int32_t prev = -1;
-    NibChunk<CW> chunk;
     chunk.clear();
     uint32_t cur = 0;   // index of the chunk being built
+    // the word the next refill takes, read an iteration ahead so that its
+    // latency overlaps the decode (reread where the slow path moves on)
+    uint32_t wv = span ? src[r.word < lastw ? r.word : lastw] : 0u;
     while (__any(active)) {
         const bool need = active && r.avail <= 32u && r.avail < r.left;
-        const uint32_t wv = span ? src[r.word < lastw ? r.word : lastw] : 0u;
         r.buf |= need ? (uint64_t)wv << (32u - r.avail) : 0u;
         r.word += need ? 1u : 0u;
         r.avail += need ? 32u : 0u;
+        wv = span ? src[r.word < lastw ? r.word : lastw] : 0u;
         const uint32_t lim = r.avail < r.left ? r.avail : r.left;
         const uint32_t x = (uint32_t)(r.buf >> 32);
         const uint32_t e1 = dist_tab[x >> (32u - kDistBits)];
@@ -562,27 +579,29 @@ __device__ __forceinline__ void decode_bucket(Src src, uint64_t start, uint64_t 
             dist = r.omega();
             sign = r.get(1);
             level = r.omega();
+            wv = span ? src[r.word < lastw ? r.word : lastw] : 0u;
         }
         // li < blen <= 2048 unless the bucket stops here (dist < 2^31)
         const uint32_t li = (uint32_t)(prev + 1) + (dist - 1u);
         const bool ins = active && r.ok && li < blen && level <= 7u;
         const uint32_t ch = li / (8u * CW);
         if (ins && ch != cur) {   // later chunks only: the chunk before is done
-            chunk.store(nib, cur, nw);
+            chunk.template store<false>(nib, cur, nw);
             chunk.clear();
             while (++cur < ch)
-                chunk.store(nib, cur, nw);
+                chunk.template store<true>(nib, cur, nw);
         }
-        chunk.put(ins ? (li >> 3) % CW : CW, ((sign << 3) | level) << (28u - 4u * (li & 7u)));
+        // every lane ORs (0 where nothing is inserted: no branch, and the
+        // word is the lane's own)
+        chunk.put((li >> 3) % CW, ins ? ((sign << 3) | level) << (28u - 4u * (li & 7u)) : 0u);
         prev = ins ? (int32_t)li : prev;
         active = ins && r.left;
     }
     // the last chunk, then zeros to the bucket's end
     if (nch) {
-        chunk.store(nib, cur, nw);
-        chunk.clear();
+        chunk.template store<false>(nib, cur, nw);
         while (++cur < nch)
-            chunk.store(nib, cur, nw);
+            chunk.template store<true>(nib, cur, nw);
     }
 }
 
@@ -595,6 +614,9 @@ __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
     __shared__ uint32_t stage[kBlockWaves][kDecodeStageWords];
     __shared__ uint16_t dist_tab[1u << kDistBits];
     __shared__ uint8_t level_tab[1u << kLevelBits];
+    constexpr uint32_t CW = Vec ? 4u : 1u;
+    __shared__ uint32_t chunk_lds[CW * kBlockThreads];
+    const LdsChunk<CW> chunk{chunk_lds + threadIdx.x};
     const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     for (uint32_t i = threadIdx.x; i < (1u << kDistBits); i += kBlockThreads)
         dist_tab[i] = (uint16_t)dist_entry(i);
@@ -645,15 +667,14 @@ __global__ __launch_bounds__(kBlockThreads) void elias_decode_kernel(
             const uint32_t blen = valid ? (uint32_t)(lo + d < n ? d : n - lo) : 0u;
             // separate calls, so that each reads through its own address space
             // (LDS reads for the staged copy, not generic loads)
-            constexpr uint32_t CW = Vec ? 4u : 1u;
             if (staged)
                 decode_bucket<CW, const uint32_t *>(
                     stage[wave] + (end > start ? (start >> 5) - wlo : 0u), start, end, blen, valid,
-                    norms + b, nibbles + (lo >> 3), dist_tab, level_tab);
+                    norms + b, nibbles + (lo >> 3), dist_tab, level_tab, chunk);
             else
                 decode_bucket<CW, const uint32_t *>(in + (start >> 5), start, end, blen, valid,
                                                     norms + b, nibbles + (lo >> 3), dist_tab,
-                                                    level_tab);
+                                                    level_tab, chunk);
         }
         __syncthreads();   // the stage is rewritten by the next group
     }
