@@ -11,19 +11,22 @@
 // significant first in 32-bit words; bit_offsets[b] is where bucket b starts
 // and bit_offsets[nb] the total length.
 //
-// Encode (d a multiple of 8, at most 2048), one wavefront per bucket, four
-// per workgroup, steps of 512 coordinates (lane L takes nibble word L):
-//   lengths -- each lane walks the non-zero nibbles of its word, its first
-//              predecessor taken from the nearest lower lane with one (a
-//              ballot and a shuffle); the wavefront sums the code lengths
-//              into the offsets array, then an exclusive scan;
+// Encode (d a multiple of 8, at most 2048): one lane per bucket, a
+// wavefront per 64 consecutive buckets.  A lane loads its bucket's nibble
+// words 512 coordinates at a time, all sixteen 16-byte blocks at once (the
+// lanes' loads are 256 bytes apart; issued together, the requests for one
+// cache line arrive together), and works on them from registers:
+//   lengths -- per nibble word, the code bits of its coordinates from
+//              popcounts, plus the omega length of its first distance; the
+//              lengths go through an exclusive scan into the offsets;
 //   zero    -- each bucket that starts inside a word clears that word (it is
 //              shared with the previous bucket);
-//   write   -- each lane codes the coordinates of its nibble word, one per
-//              pass of a per-lane loop, at the bit position a wavefront scan
-//              of the lanes' code lengths gives it; codes are ORed into the
-//              bucket's bits in LDS, which leave as plain stores (atomic ORs
-//              for the two words a bucket may share).
+//   write   -- block by block (32 coordinates), each lane appends the codes
+//              of its coded coordinates to a 64-bit window and hands each
+//              completed word to the wavefront's LDS stage (an OR: a word two
+//              buckets share gets both), which leaves with coalesced stores;
+//              a wavefront whose words exceed the stage stores directly,
+//              atomic ORs on the shared words.
 // Decode: one lane per bucket (variable-length codes are read in order), a
 // wavefront per 64 consecutive buckets.  Their bits, one contiguous range,
 // are first copied into LDS with coalesced loads; each coordinate is then
@@ -96,32 +99,6 @@ __device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w)
     return (w | (w >> 1) | (w >> 2)) & 0x11111111u;
 }
 
-// The lane's nibble word of the step starting at coordinate c0, with the
-// coordinates at or past the bucket's length cleared.
-__device__ __forceinline__ uint32_t step_word(const uint32_t *__restrict__ nibbles, uint64_t lo,
-                                              uint32_t li0, uint32_t blen)
-{
-    if (li0 >= blen)
-        return 0u;
-    uint32_t w = nibbles[(lo + li0) >> 3];
-    if (li0 + 8u > blen)
-        w &= ~0u << (4u * (li0 + 8u - blen));
-    return w;
-}
-
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, uint32_t lane)
-{
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, kWave);
-        if (lane >= (uint32_t)off)
-            x += y;
-    }
-    return x;
-}
-
-constexpr uint32_t kEliasStep = 8u * kWave;   // coordinates per wavefront step
-
 // Coded coordinates of a nibble word as an 8-bit mask, coordinate j of the
 // word in bit 7 - j (so the previous coordinate is one bit higher).
 __device__ __forceinline__ uint32_t coord_mask8(uint32_t w)
@@ -154,68 +131,87 @@ __device__ __forceinline__ uint32_t word_code_bits(uint32_t w, uint32_t m8)
     return bits;
 }
 
-// The bits of one step's nibble word (lane-local), with the predecessor of
-// its first coded coordinate taken from the nearest lower lane that has one,
-// or from earlier steps (prev); prev moves to the step's last coded one.
-struct StepWord {
-    uint32_t w, m8, bits;
-    int32_t pred;   // coordinate before the word's first coded one (-1: none)
-};
+// Encode: one lane per bucket, a wavefront per 64 consecutive buckets (the
+// decode's layout).  A lane reads its bucket's nibble words in order, 16
+// bytes at a time with the next 16 in flight.
 
-__device__ __forceinline__ StepWord step_bits(uint32_t w, uint32_t li0, uint32_t lane,
-                                              int32_t &prev)
+// Block k (words 4k .. 4k+3) of a bucket of nw nibble words at p, zeros
+// past nw.  Vec: p is 16-byte aligned, and a block wholly inside the
+// bucket is one 16-byte load; other blocks are read word by word.
+template <bool Vec>
+__device__ __forceinline__ uint4 nib_block(const uint32_t *__restrict__ p, uint32_t k, uint32_t nw)
 {
-    StepWord sw;
-    sw.w = w;
-    sw.m8 = coord_mask8(w);
-    const int32_t first = (int32_t)(li0 + (uint32_t)__builtin_clz(sw.m8 | 1u) - 24u);
-    const int32_t last = sw.m8 ? (int32_t)(li0 + 7u - (uint32_t)__builtin_ctz(sw.m8)) : -1;
-    const uint64_t any = __ballot(sw.m8 != 0u);
-    const uint64_t below = any & ((1ull << lane) - 1ull);
-    const int32_t from_below = __shfl(last, below ? 63 - (int)__builtin_clzll(below) : 0, kWave);
-    sw.pred = below ? from_below : prev;
-    sw.bits = sw.m8 ? word_code_bits(w, sw.m8) + omega_len_fast((uint32_t)(first - sw.pred)) : 0u;
-    if (any)
-        prev = __shfl(last, 63 - (int)__builtin_clzll(any), kWave);
-    return sw;
+    const uint32_t w0 = 4u * k;
+    if (Vec && w0 + 4u <= nw)
+        return reinterpret_cast<const uint4 *>(p)[k];
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (w0 < nw)
+        v.x = p[w0];
+    if (w0 + 1u < nw)
+        v.y = p[w0 + 1u];
+    if (w0 + 2u < nw)
+        v.z = p[w0 + 2u];
+    if (w0 + 3u < nw)
+        v.w = p[w0 + 3u];
+    return v;
 }
 
-constexpr int kEliasBlocksPerCU = 8;   // grid-stride workgroups per compute unit
+// Nibble word j of a bucket of blen coordinates, the coordinates at or past
+// blen cleared.
+__device__ __forceinline__ uint32_t clip_word(uint32_t w, uint32_t j, uint32_t blen)
+{
+    const uint32_t li0 = 8u * j;
+    if (li0 + 8u <= blen)
+        return w;
+    return li0 < blen ? w & (~0u << (4u * (li0 + 8u - blen))) : 0u;
+}
 
+__device__ __forceinline__ uint32_t word_of(uint4 v, uint32_t q)   // word q (0..3) of a block
+{
+    return q == 0u ? v.x : q == 1u ? v.y : q == 2u ? v.z : v.w;
+}
+
+// Bucket lengths in bits: the norm's 32, then per nibble word the code bits
+// of its coordinates (word_code_bits) and the omega length of its first
+// coordinate's distance from the lane's previous coded coordinate.
+template <bool Vec>
 __global__ __launch_bounds__(kBlockThreads) void elias_length_kernel(
     const uint32_t *__restrict__ nibbles, uint64_t n, uint32_t d, uint64_t nb,
     uint64_t *__restrict__ offs)
 {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint64_t wstride = (uint64_t)gridDim.x * kBlockWaves;
-    uint64_t b = (uint64_t)blockIdx.x * kBlockWaves + threadIdx.x / kWave;
-    // the first word of the next bucket is loaded one bucket ahead
-    uint32_t w_next = 0;
-    if (b < nb) {
-        const uint64_t lo = b * d;
-        w_next = step_word(nibbles, lo, 8u * lane, (uint32_t)(lo + d < n ? d : n - lo));
-    }
-    for (; b < nb; b += wstride) {
-        const uint64_t lo = b * d;
-        const uint32_t blen = (uint32_t)(lo + d < n ? d : n - lo);
-        const uint32_t w0 = w_next;
-        if (b + wstride < nb) {
-            const uint64_t lo2 = (b + wstride) * d;
-            w_next = step_word(nibbles, lo2, 8u * lane, (uint32_t)(lo2 + d < n ? d : n - lo2));
-        }
-        int32_t prev = -1;
-        uint32_t bits = 0;
-        for (uint32_t c0 = 0; c0 < blen; c0 += kEliasStep) {
-            const uint32_t li0 = c0 + 8u * lane;
-            const uint32_t w = c0 ? step_word(nibbles, lo, li0, blen) : w0;
-            bits += step_bits(w, li0, lane, prev).bits;
-        }
+    const uint64_t b = (uint64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+    if (b >= nb)
+        return;
+    const uint64_t lo = b * d;
+    const uint32_t blen = (uint32_t)(lo + d < n ? d : n - lo);
+    const uint32_t nw = (blen + 7u) / 8u;
+    const uint32_t nblk = (nw + 3u) / 4u;
+    const uint32_t *p = nibbles + (lo >> 3);
+    uint32_t bits = 32u;
+    int32_t prev = -1;
+    // 512 coordinates at a time: their 16 blocks loaded together
+    constexpr uint32_t kB = 16;
+    for (uint32_t k0 = 0; k0 < nblk; k0 += kB) {
+        uint4 blk[kB];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            bits += __shfl_xor(bits, off, kWave);
-        if (lane == 0)
-            offs[b] = 32u + bits;
+        for (uint32_t t = 0; t < kB; ++t)
+            blk[t] = k0 + t < nblk ? nib_block<Vec>(p, k0 + t, nw) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (uint32_t t = 0; t < kB; ++t) {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                const uint32_t j = 4u * (k0 + t) + q;
+                const uint32_t w = clip_word(word_of(blk[t], q), j, blen);
+                const uint32_t m8 = coord_mask8(w);
+                const int32_t first = (int32_t)(8u * j + (uint32_t)__builtin_clz(m8 | 1u) - 24u);
+                const int32_t gap = first - prev > 1 ? first - prev : 1;   // >= 1 when m8 != 0
+                const uint32_t add = word_code_bits(w, m8) + omega_len_fast((uint32_t)gap);
+                bits += m8 ? add : 0u;
+                prev = m8 ? (int32_t)(8u * j + 7u - (uint32_t)__builtin_ctz(m8)) : prev;
+            }
+        }
     }
+    offs[b] = bits;
 }
 
 __global__ __launch_bounds__(kBlockThreads) void elias_zero_kernel(const uint64_t *__restrict__ offs,
@@ -231,121 +227,151 @@ __global__ __launch_bounds__(kBlockThreads) void elias_zero_kernel(const uint64_
     }
 }
 
-// LDS: the omega codes of 1..d ((length << 24) | code, one word each,
-// shared by the workgroup), then per wavefront the bucket's bits
-// (region_words words: the start's shift, the norm, every coordinate at its
-// longest code, and the word a code may spill into).  Each lane codes the
-// coordinates of its nibble word at the position a wavefront scan of the
-// lanes' code lengths gives it; a bucket's offsets, inputs and first words
-// are loaded one group ahead.
-struct WriteFetch {
-    uint64_t start, end;
-    uint32_t norm_bits, w0;
-};
+// Staged output words per wavefront (as the decode stages its input): with
+// the omega table of 1..d, four workgroups fit a compute unit for d <= 2048.
+constexpr uint32_t kEncodeStageWords = 31u * kWave;
 
-__device__ __forceinline__ WriteFetch write_fetch(const float *__restrict__ norms,
-                                                  const uint32_t *__restrict__ nibbles,
-                                                  const uint64_t *__restrict__ offs, uint64_t n,
-                                                  uint32_t d, uint64_t nb, uint64_t b,
-                                                  uint32_t lane)
-{
-    WriteFetch f{0u, 0u, 0u, 0u};
-    if (b < nb) {
-        const uint64_t lo = b * d;
-        f.start = offs[b];
-        f.end = offs[b + 1];
-        f.norm_bits = __float_as_uint(norms[b]);
-        f.w0 = step_word(nibbles, lo, 8u * lane, (uint32_t)(lo + d < n ? d : n - lo));
-    }
-    return f;
-}
-
+// The code words.  LDS: the omega codes of 1..d ((length << 24) | code, one
+// word each, shared by the workgroup), then per wavefront the stage of its
+// 64 buckets' words.  Each lane appends its bucket's codes to a 64-bit
+// window (next free bit `fill` of word wi) and hands each word on as it
+// completes: ORed into the stage, which the wavefront then stores with
+// coalesced stores, or, when the wavefront's words do not fit the stage,
+// stored directly.  A word two buckets share is ORed by both: in the stage,
+// or, in memory, with an atomic OR on the word the zero kernel cleared.
+template <bool Vec>
 __global__ __launch_bounds__(kBlockThreads) void elias_write_kernel(
     const float *__restrict__ norms, const uint32_t *__restrict__ nibbles, uint64_t n, uint32_t d,
-    uint64_t nb, const uint64_t *__restrict__ offs, uint32_t *__restrict__ out, uint64_t cap,
-    uint32_t region_words)
+    uint64_t nb, const uint64_t *__restrict__ offs, uint32_t *__restrict__ out, uint64_t cap)
 {
     extern __shared__ uint32_t elias_lds[];
     const uint32_t lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t *codes = elias_lds;
-    uint32_t *bits = elias_lds + (d + 1u) + wave * region_words;
+    uint32_t *stage = elias_lds + (d + 1u) + wave * kEncodeStageWords;
     for (uint32_t k = threadIdx.x + 1u; k <= d; k += kBlockThreads) {
         uint32_t len;
         const uint32_t c = omega_code_fast(k, len);
         codes[k] = (len << 24) | c;
     }
-    const uint64_t ngroups = (nb + kBlockWaves - 1) / kBlockWaves;
-    uint64_t grp = blockIdx.x;
-    WriteFetch next = write_fetch(norms, nibbles, offs, n, d, nb, grp * kBlockWaves + wave, lane);
-    for (; grp < ngroups; grp += gridDim.x) {
-        const uint64_t b = grp * kBlockWaves + wave;
-        const bool valid = b < nb;
-        const WriteFetch cur = next;
-        if (grp + gridDim.x < ngroups)
-            next = write_fetch(norms, nibbles, offs, n, d, nb, (grp + gridDim.x) * kBlockWaves + wave,
-                               lane);
-        const uint64_t lo = b * d;
-        const uint32_t blen = valid ? (uint32_t)(lo + d < n ? d : n - lo) : 0u;
-        const uint32_t sh = (uint32_t)(cur.start & 31u);
-        uint64_t nwl = valid ? ((uint64_t)sh + (cur.end - cur.start) + 31u) / 32u + 1u : 0u;
-        nwl = nwl < region_words ? nwl : region_words;
-        for (uint32_t k = lane; k < nwl; k += kWave)
-            bits[k] = 0u;
-        __syncthreads();   // the cleared bits (and, the first time, the code table)
-        if (valid && lane == 0) {
-            const uint64_t v = (uint64_t)cur.norm_bits << (32u - sh);
-            atomicOr(&bits[0], (uint32_t)(v >> 32));
-            atomicOr(&bits[1], (uint32_t)v);
-        }
-        int32_t prev = -1;
-        uint32_t pos = sh + 32u;   // region bit position of the step's first code
-        for (uint32_t c0 = 0; c0 < blen; c0 += kEliasStep) {
-            const uint32_t li0 = c0 + 8u * lane;
-            const StepWord sw =
-                step_bits(c0 ? step_word(nibbles, lo, li0, blen) : cur.w0, li0, lane, prev);
-            const uint32_t incl = wave_inclusive_scan(sw.bits, lane);
-            uint32_t q = pos + incl - sw.bits;
-            pos += __shfl(incl, kWave - 1, kWave);
-            uint32_t m = sw.m8;
-            int32_t p = sw.pred;
-            while (m) {
-                const uint32_t h = 31u - (uint32_t)__builtin_clz(m);   // coordinate 7 - h
-                const uint32_t idx = li0 + 7u - h;
-                const uint32_t nibv = (sw.w >> (4u * h)) & 15u;
-                const uint32_t cd = codes[(uint32_t)((int32_t)idx - p)];
-                const uint32_t cl = codes[nibv & 7u];
-                const uint32_t llen = cl >> 24;
-                const uint32_t code =
-                    ((((cd & 0xFFFFFFu) << 1) | (nibv >> 3)) << llen) | (cl & 0xFFFFFFu);
-                const uint32_t len = (cd >> 24) + 1u + llen;   // <= 26 bits
-                // q + len stays inside the bucket's region by construction (the
-                // lengths are the ones that made the offsets); checked anyway
-                const uint32_t wd = q >> 5, o = q & 31u;
-                if (wd + 1u < region_words) {
-                    const uint64_t v = (uint64_t)code << (64u - len - o);
-                    atomicOr(&bits[wd], (uint32_t)(v >> 32));
-                    if ((uint32_t)v)
-                        atomicOr(&bits[wd + 1], (uint32_t)v);
-                }
-                q += len;
-                p = (int32_t)idx;
-                m &= ~(1u << h);
-            }
-        }
-        __syncthreads();   // every code is in
-        const uint64_t nw = valid ? ((uint64_t)sh + (cur.end - cur.start) + 31u) >> 5 : 0u;
-        const bool shares_last = ((cur.end & 31u) != 0u) && (b + 1 < nb);
-        for (uint64_t k = lane; k < nw; k += kWave) {
-            const uint64_t gw = (cur.start >> 5) + k;
-            if (gw >= cap)
-                continue;
-            const uint32_t v = bits[k];
-            if ((k == 0 && sh) || (k == nw - 1 && shares_last))
-                atomicOr(&out[gw], v);
+    __syncthreads();
+    const uint64_t b0 = ((uint64_t)blockIdx.x * kBlockWaves + wave) * kWave;
+    if (b0 >= nb)
+        return;   // (no barrier below)
+    const uint64_t b = b0 + lane;
+    const bool valid = b < nb;
+    const uint32_t last = (uint32_t)(nb - b0 < kWave ? nb - b0 - 1u : kWave - 1u);
+    uint64_t start = 0, end = 0;
+    if (valid) {
+        start = offs[b];
+        end = offs[b + 1];
+    }
+    // the wavefront's words [wlo, whi): its buckets are consecutive
+    const uint64_t s0 = __shfl(start, 0, kWave);
+    const uint64_t e_last = __shfl(end, (int)last, kWave);
+    const uint64_t wlo = s0 >> 5, whi = (e_last + 31u) >> 5;
+    const bool staged = whi - wlo <= kEncodeStageWords;
+    if (staged)
+        for (uint64_t k = lane; k < whi - wlo; k += kWave)
+            stage[k] = 0u;
+    // LDS operations of a wavefront take effect in order; keep the compiler
+    // from moving the ORs below above the clears
+    __builtin_amdgcn_wave_barrier();
+    const bool share_first = (start & 31u) != 0u;
+    const bool share_last = (end & 31u) != 0u && b + 1 < nb;
+    auto emit = [&](uint64_t gw, uint32_t v) {
+        if (staged) {
+            __hip_atomic_fetch_or(stage + (gw - wlo), v, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else if (gw < cap) {
+            if ((gw == (start >> 5) && share_first) || (gw == ((end - 1u) >> 5) && share_last))
+                atomicOr(out + gw, v);
             else
                 out[gw] = v;
         }
-        __syncthreads();   // the bits are cleared for the next group
+    };
+    const uint64_t lo = valid ? b * d : 0u;
+    const uint32_t blen = valid ? (uint32_t)(lo + d < n ? d : n - lo) : 0u;
+    const uint32_t nw = (blen + 7u) / 8u;
+    const uint32_t *p = nibbles + (lo >> 3);
+    uint64_t wi = start >> 5;
+    uint32_t fill = (uint32_t)(start & 31u);
+    uint64_t acc = 0;
+    if (valid) {   // the norm's 32 bits complete the first word
+        acc = (uint64_t)__float_as_uint(norms[b]) << (32u - fill);
+        emit(wi, (uint32_t)(acc >> 32));
+        acc <<= 32;
+        ++wi;
+    }
+    // 512 coordinates at a time: their 16 blocks of nibble words loaded
+    // together, then coded block by block; within a block each lane takes its
+    // coded coordinates in order (coordinate c of the block at bit 31 - c of
+    // m32, its nibble in the 64-bit half c / 16)
+    constexpr uint32_t kB = 16;
+    const uint32_t nblk = (nw + 3u) / 4u;
+    const uint32_t nblk_full = (d / 8u + 3u) / 4u;   // any bucket's, wave-uniform
+    int32_t prev = -1;
+    for (uint32_t k0 = 0; k0 < nblk_full; k0 += kB) {
+        uint4 blk[kB];
+#pragma unroll
+        for (uint32_t t = 0; t < kB; ++t)
+            blk[t] = k0 + t < nblk ? nib_block<Vec>(p, k0 + t, nw) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (uint32_t t = 0; t < kB; ++t) {
+            const uint32_t k = k0 + t;
+            if (k >= nblk_full)
+                continue;   // (wave-uniform)
+            const uint32_t w0 = clip_word(blk[t].x, 4u * k, blen);
+            const uint32_t w1 = clip_word(blk[t].y, 4u * k + 1u, blen);
+            const uint32_t w2 = clip_word(blk[t].z, 4u * k + 2u, blen);
+            const uint32_t w3 = clip_word(blk[t].w, 4u * k + 3u, blen);
+            const uint64_t hi = ((uint64_t)w0 << 32) | w1, lo = ((uint64_t)w2 << 32) | w3;
+            uint32_t m32 = (coord_mask8(w0) << 24) | (coord_mask8(w1) << 16) |
+                           (coord_mask8(w2) << 8) | coord_mask8(w3);
+            while (__any(m32 != 0u)) {
+                if (m32) {
+                    const uint32_t c = (uint32_t)__builtin_clz(m32);
+                    const uint32_t li = 32u * k + c;
+                    const uint32_t nibv =
+                        (uint32_t)((c < 16u ? hi : lo) >> (60u - 4u * (c & 15u))) & 15u;
+                    const uint32_t cd = codes[(uint32_t)((int32_t)li - prev)];   // in [1, d]
+                    const uint32_t cl = codes[nibv & 7u];                         // level 1..7
+                    const uint32_t llen = cl >> 24;
+                    const uint32_t code =
+                        ((((cd & 0xFFFFFFu) << 1) | (nibv >> 3)) << llen) | (cl & 0xFFFFFFu);
+                    const uint32_t len = (cd >> 24) + 1u + llen;   // <= 26 bits
+                    acc |= (uint64_t)code << (64u - fill - len);
+                    fill += len;
+                    prev = (int32_t)li;
+                    m32 &= ~(0x80000000u >> c);
+                    if (fill >= 32u) {
+                        emit(wi, (uint32_t)(acc >> 32));
+                        acc <<= 32;
+                        fill -= 32u;
+                        ++wi;
+                    }
+                }
+            }
+        }
+    }
+    if (valid && fill)   // the last, partial word
+        emit(wi, (uint32_t)(acc >> 32));
+    __builtin_amdgcn_wave_barrier();
+    if (staged) {
+        // the wavefront's first and last words may be shared with the
+        // neighbouring wavefronts' buckets
+        const uint64_t nwords = whi - wlo;
+        const bool first_shared = (s0 & 31u) != 0u;
+        const bool last_shared = (e_last & 31u) != 0u && b0 + last + 1 < nb;
+        for (uint64_t k = lane; k < nwords; k += kWave) {
+            const uint64_t gw = wlo + k;
+            if (gw >= cap)
+                continue;
+            const uint32_t v = stage[k];
+            if ((k == 0 && first_shared) || (k == nwords - 1u && last_shared))
+                atomicOr(out + gw, v);
+            else
+                out[gw] = v;
+        }
     }
 }
 
@@ -697,10 +723,14 @@ hipError_t launch_elias_encode(const float *norms, const uint32_t *nibbles, uint
                                uint64_t *offs, uint32_t *out, uint64_t cap, hipStream_t stream)
 {
     const uint64_t nb = (n + d - 1) / d;
-    const uint64_t ngroups = (nb + kBlockWaves - 1) / kBlockWaves;
+    // 16-byte nibble loads when every bucket starts 16-byte aligned
+    const bool vec = d % 32u == 0 && ((uintptr_t)nibbles & 15u) == 0;
+    const uint32_t grid = grid_for((nb + kBlockThreads - 1) / kBlockThreads, 0);
     if (nb) {
-        elias_length_kernel<<<grid_for(ngroups, kEliasBlocksPerCU), kBlockThreads, 0, stream>>>(
-            nibbles, n, d, nb, offs);
+        if (vec)
+            elias_length_kernel<true><<<grid, kBlockThreads, 0, stream>>>(nibbles, n, d, nb, offs);
+        else
+            elias_length_kernel<false><<<grid, kBlockThreads, 0, stream>>>(nibbles, n, d, nb, offs);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -708,17 +738,17 @@ hipError_t launch_elias_encode(const float *norms, const uint32_t *nibbles, uint
     hipError_t e = launch_exclusive_scan_u64(offs, nb, stream);
     if (e != hipSuccess || !nb)
         return e;
-    elias_zero_kernel<<<grid_for((nb + kBlockThreads - 1) / kBlockThreads, 0), kBlockThreads, 0,
-                        stream>>>(offs, nb, out, cap);
+    elias_zero_kernel<<<grid, kBlockThreads, 0, stream>>>(offs, nb, out, cap);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    // bits of one bucket: shift + norm + every coordinate at its longest
-    // code, plus the word a code may spill into
-    const uint32_t region_words = (31u + 32u + d * max_coord_bits(d) + 31u) / 32u + 1u;
-    const size_t lds = ((size_t)d + 1u + (size_t)kBlockWaves * region_words) * 4u;
-    elias_write_kernel<<<grid_for(ngroups, kEliasBlocksPerCU), kBlockThreads, lds, stream>>>(
-        norms, nibbles, n, d, nb, offs, out, cap, region_words);
+    const size_t lds = ((size_t)d + 1u + (size_t)kBlockWaves * kEncodeStageWords) * 4u;
+    if (vec)
+        elias_write_kernel<true><<<grid, kBlockThreads, lds, stream>>>(norms, nibbles, n, d, nb,
+                                                                        offs, out, cap);
+    else
+        elias_write_kernel<false><<<grid, kBlockThreads, lds, stream>>>(norms, nibbles, n, d, nb,
+                                                                         offs, out, cap);
     return hipGetLastError();
 }
 

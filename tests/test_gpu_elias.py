@@ -109,6 +109,37 @@ def test_capacity_and_guard_words(gpu):
         assert np.all(o[cap:] == 0x5A5A5A5A), cap
 
 
+def test_wavefronts_past_the_stage(gpu):
+    # a wavefront codes 64 consecutive buckets; when their words exceed its
+    # LDS stage (1984 words) each lane stores its words itself: dense buckets
+    # of 129+ words each, mixed with sparse ones, at several capacities
+    import torch
+
+    say("elias unstaged wavefronts")
+    rs = np.random.default_rng(113)
+    for d in (512, 256):
+        nb = 3 * 64 + 7
+        n = nb * d - 3
+        nib = rs.integers(0, 1 << 32, (n + 7) // 8, dtype=np.uint64).astype(np.uint32)
+        dense = rs.uniform(size=nb) < 0.7
+        for bk in range(nb):
+            w0, w1 = bk * d // 8, min((bk + 1) * d // 8, nib.size)
+            if dense[bk]:
+                nib[w0:w1] |= np.uint32(0x11111111)
+            else:
+                nib[w0:w1] &= np.uint32(0x88888888) | (nib[w0:w1] >> np.uint32(5)) & np.uint32(0x01000100)
+        norms = rs.uniform(0.1, 3, nb).astype(np.float32)
+        check(gpu, norms, nib, n, d)
+        offs_h, words_h = oracle.qsgd_elias_encode(norms, nib, n, d)
+        for cap in (words_h.size // 3, 4097):
+            out = torch.full((words_h.size + 64,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+            offs = torch.empty(offs_h.size, dtype=torch.int64, device="cuda")
+            gpu.qsgd_elias_encode(dev(norms), dev(nib), n, d, offsets=offs, out=out[:cap])
+            o = host(out)
+            assert np.array_equal(o[:cap], words_h[:cap]), (d, cap)
+            assert np.all(o[cap:] == 0x5A5A5A5A), (d, cap)
+
+
 def test_round_trip_on_gpu(gpu):
     say("elias gpu round trip")
     rs = np.random.default_rng(112)
