@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kBlockThreads) void elias_write_kernel(
             const uint32_t w1 = clip_word(blk[t].y, 4u * k + 1u, blen);
             const uint32_t w2 = clip_word(blk[t].z, 4u * k + 2u, blen);
             const uint32_t w3 = clip_word(blk[t].w, 4u * k + 3u, blen);
-            const uint64_t hi = ((uint64_t)w0 << 32) | w1, lo = ((uint64_t)w2 << 32) | w3;
+            const uint64_t half0 = ((uint64_t)w0 << 32) | w1, half1 = ((uint64_t)w2 << 32) | w3;
             uint32_t m32 = (coord_mask8(w0) << 24) | (coord_mask8(w1) << 16) |
                            (coord_mask8(w2) << 8) | coord_mask8(w3);
             while (__any(m32 != 0u)) {
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kBlockThreads) void elias_write_kernel(
                     const uint32_t c = (uint32_t)__builtin_clz(m32);
                     const uint32_t li = 32u * k + c;
                     const uint32_t nibv =
-                        (uint32_t)((c < 16u ? hi : lo) >> (60u - 4u * (c & 15u))) & 15u;
+                        (uint32_t)((c < 16u ? half0 : half1) >> (60u - 4u * (c & 15u))) & 15u;
                     const uint32_t cd = codes[(uint32_t)((int32_t)li - prev)];   // in [1, d]
                     const uint32_t cl = codes[nibv & 7u];                         // level 1..7
                     const uint32_t llen = cl >> 24;

@@ -152,6 +152,25 @@ def test_round_trip_on_gpu(gpu):
     assert np.array_equal(host(nib2), clear_zero_level_signs(host(nib_d)))
 
 
+def test_encode_from_unaligned_nibbles(gpu):
+    # d a multiple of 32 with nibbles that are 4- but not 16-byte aligned: the
+    # encoder reads word by word instead of 16-byte blocks
+    import torch
+
+    say("elias encode, unaligned nibbles")
+    rs = np.random.default_rng(115)
+    for d in (256, 512):
+        n = 70 * d + 77
+        g = (rs.standard_normal(n) * 0.01).astype(np.float32)
+        norms, nib = oracle.qsgd_quantize(g, d, 7, 51 + d)
+        offs_h, words_h = oracle.qsgd_elias_encode(norms, nib, n, d)
+        buf = torch.zeros(nib.size + 4, dtype=torch.int32, device="cuda")
+        buf[1:1 + nib.size] = dev(nib)
+        offs, out = gpu.qsgd_elias_encode(dev(norms), buf[1:1 + nib.size], n, d)
+        assert np.array_equal(host(offs).astype(np.uint64), offs_h), d
+        assert np.array_equal(host(out)[:words_h.size], words_h), d
+
+
 def _bits(words, lo, hi):
     w = np.ascontiguousarray(words).astype(">u4").view(np.uint8)
     return np.unpackbits(w)[lo:hi]
