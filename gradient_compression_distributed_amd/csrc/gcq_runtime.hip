@@ -56,7 +56,10 @@ void init_locked()
     if (g_tuning.qsgd_buckets_per_wave != 1 && g_tuning.qsgd_buckets_per_wave != 2 &&
         g_tuning.qsgd_buckets_per_wave != 4)
         g_tuning.qsgd_buckets_per_wave = 0;
-    g_tuning.dq_words_per_thread = env_int("GCQ_DQ_WORDS_PER_THREAD", 2) == 1 ? 1 : 2;
+    {
+        const int wpt = env_int("GCQ_DQ_WORDS_PER_THREAD", 0);
+        g_tuning.dq_words_per_thread = wpt == 1 || wpt == 2 ? wpt : 0;
+    }
     g_tuning.dq_resident_per_cu = env_int("GCQ_DQ_RESIDENT_PER_CU", 3);
     if (!resident_ok(g_tuning.dq_resident_per_cu))
         g_tuning.dq_resident_per_cu = 3;
@@ -93,7 +96,7 @@ bool tuning_valid(const gcq_tuning &t)
            count_ok(t.qsgd_dequant_blocks_per_cu) &&
            (t.qsgd_buckets_per_wave == 0 || t.qsgd_buckets_per_wave == 1 ||
             t.qsgd_buckets_per_wave == 2 || t.qsgd_buckets_per_wave == 4) &&
-           (t.dq_words_per_thread == 1 || t.dq_words_per_thread == 2) &&
+           (t.dq_words_per_thread >= 0 && t.dq_words_per_thread <= 2) &&
            resident_ok(t.dq_resident_per_cu) && resident_ok(t.gc2_resident_per_cu) &&
            resident_ok(t.cdsgd_resident_per_cu) && resident_ok(t.qsgd_avg_resident_per_cu);
 }

@@ -527,8 +527,10 @@ typedef struct gcq_tuning {
                                lanes: 1, 2 or 4, limited to d H <= 1024; 0:
                                H = 1024/d for d <= 1024, else 1 (default) */
     int dq_words_per_thread; /* gc2_dequant_reduce: packed words per thread,
-                               1 or 2 (default: 8-byte loads, used when every
-                               worker array is 8-byte aligned, else 1) */
+                               1 or 2 (8-byte loads, used when every worker
+                               array is 8-byte aligned, else 1); 0: 2 from
+                               2^22 words (2^26 elements) per launch, else 1
+                               (default) */
     int dq_resident_per_cu; /* gc2_dequant_reduce: at most this many
                                workgroups resident per compute unit, set through
                                the kernel's LDS allocation: 0 (no cap) or 2..8
@@ -561,7 +563,7 @@ typedef struct gcq_tuning {
  * another call of this library.  Errors: GCQ_ERR_NULL, GCQ_ERR_PARAM (a
  * flag not 0/1, gc2_nt outside 0..15, gc2_unroll not 1/2/4, a block
  * count outside 0..1024, qsgd_buckets_per_wave not 0/1/2/4,
- * dq_words_per_thread not 1/2, a *_resident_per_cu knob not 0 or 2..8); on
+ * dq_words_per_thread not 0..2, a *_resident_per_cu knob not 0 or 2..8); on
  * error
  * nothing changes.
  */

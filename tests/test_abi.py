@@ -311,7 +311,7 @@ def test_tuning_roundtrip_and_validation(lib):
                        ("qsgd_rcp", 2), ("qsgd_dequant_nt", 3), ("dq_fp4_decode", 2),
                        ("qsgd_blocks_per_cu", -1), ("qsgd_dequant_blocks_per_cu", 1025),
                        ("qsgd_buckets_per_wave", 3), ("qsgd_buckets_per_wave", -1),
-                       ("dq_words_per_thread", 3), ("dq_words_per_thread", 0),
+                       ("dq_words_per_thread", 3), ("dq_words_per_thread", -1),
                        ("dq_resident_per_cu", 1), ("dq_resident_per_cu", 9),
                        ("dq_resident_per_cu", -1), ("gc2_resident_per_cu", 1),
                        ("gc2_resident_per_cu", 9), ("cdsgd_resident_per_cu", 1),
@@ -376,7 +376,7 @@ def test_element_limit(lib):
 DEFAULTS = {"gc2_unroll": 1, "gc2_nt": 7, "gc2_blocks_per_cu": 0, "dq_nt_loads": 1,
             "dq_nt_stores": 1, "dq_lds_stores": 1, "dq_blocks_per_cu": 0, "dq_fp4_decode": 1,
             "qsgd_nt": 1, "qsgd_rcp": 1, "qsgd_dequant_nt": 1, "qsgd_blocks_per_cu": 0,
-            "qsgd_dequant_blocks_per_cu": 0, "qsgd_buckets_per_wave": 0, "dq_words_per_thread": 2,
+            "qsgd_dequant_blocks_per_cu": 0, "qsgd_buckets_per_wave": 0, "dq_words_per_thread": 0,
             "dq_resident_per_cu": 3, "gc2_resident_per_cu": 0, "cdsgd_resident_per_cu": 5,
             "qsgd_avg_resident_per_cu": 0}
 

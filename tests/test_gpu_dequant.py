@@ -51,7 +51,8 @@ DQ_VARIANTS = [dict(dq_nt_loads=l, dq_nt_stores=s, dq_lds_stores=d, dq_blocks_pe
                                              (1, 1, 1, 8, 0, 1, 2), (0, 1, 0, 0, 1, 1, 4),
                                              (1, 1, 1, 0, 1, 2, 2), (0, 0, 1, 3, 0, 2, 0),
                                              (1, 0, 1, 0, 1, 2, 3), (0, 1, 1, 0, 0, 2, 8),
-                                             (1, 1, 1, 0, 1, 2, 0), (1, 1, 1, 2, 1, 2, 2)]]
+                                             (1, 1, 1, 0, 1, 2, 0), (1, 1, 1, 2, 1, 2, 2),
+                                             (1, 1, 1, 0, 1, 0, 3)]]
 
 
 @pytest.mark.parametrize("var", range(len(DQ_VARIANTS)))
