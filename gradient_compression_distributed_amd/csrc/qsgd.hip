@@ -235,6 +235,56 @@ __device__ __forceinline__ bool group_any(bool p, uint32_t grp)
         return ((m >> (grp * G)) & ((1ull << G) - 1u)) != 0;
 }
 
+// The last bucket when it is shorter than the fused kernel's D (elements
+// e0 .. n - 1, e0 a multiple of 8), after the fused kernel: one wavefront,
+// norm and nibbles in one launch, with the arithmetic of the generic kernels
+// below (lanes stride the bucket for the float64 sum of squares or the
+// largest magnitude; lanes stride its nibble words, each element taking the
+// level as defined).
+template <bool Max>
+__global__ __launch_bounds__(kWave) void qsgd_tail_kernel(const float *__restrict__ g, uint64_t n,
+                                                           uint64_t e0, uint64_t b, uint32_t s,
+                                                           uint32_t k0, uint32_t k1,
+                                                           float *__restrict__ norms,
+                                                           uint32_t *__restrict__ nib)
+{
+    const uint32_t lane = threadIdx.x;
+    float norm;
+    if constexpr (Max) {
+        float m = 0.0f;
+        for (uint64_t e = e0 + lane; e < n; e += kWave)
+            m = max_in(m, fabsf(g[e]));
+        norm = group_max<kWave>(m);
+    } else {
+        double ss = 0.0;
+        for (uint64_t e = e0 + lane; e < n; e += kWave)
+            ss = __builtin_fma((double)g[e], (double)g[e], ss);
+        ss = group_sum<kWave>(ss);
+        norm = bucket_norm(ss);
+    }
+    if (lane == 0)
+        norms[b] = norm;
+    const float sf = (float)s;
+    const uint64_t w1 = (n + 7) >> 3;
+    for (uint64_t w = (e0 >> 3) + lane; w < w1; w += kWave) {
+        uint32_t word = 0;
+#pragma unroll
+        for (uint32_t half = 0; half < 2; ++half) {
+            const uint64_t eb = (w << 3) + 4u * half;
+            float u[4];
+            uniforms4(eb >> 2, k0, k1, u);
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                const uint64_t e = eb + q;
+                if (e < n)
+                    word |= (sign_bit(g[e]) | qsgd_level_exact(fabsf(g[e]), norm, sf, s, u[q]))
+                            << (28u - 4u * (4u * half + q));
+            }
+        }
+        nib[w] = word;
+    }
+}
+
 // Fused norm + levels + nibbles for buckets of D = 256*C elements held in
 // registers.  A wavefront owns H consecutive buckets at a time, one per
 // aligned group of G = 64/H lanes; lane l of a group holds elements
@@ -865,9 +915,10 @@ __global__ __launch_bounds__(kBlockThreads) void qsgd_average_generic_kernel(
 }
 
 template <int CC, int H, bool Max>
-void launch_fused(const gcq_tuning &tu, const float *g, uint32_t s, uint32_t k0, uint32_t k1,
-                  float *norms, uint32_t *nibbles, uint64_t nb_done, hipStream_t stream)
+void launch_fused(const gcq_tuning &tu, const float *g, uint64_t n, uint32_t s, uint32_t k0,
+                  uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done, hipStream_t stream)
 {
+    constexpr uint64_t D = 256u * CC;
     const uint64_t waves = (nb_done + H - 1) / H;
     const uint32_t grid = grid_for((waves + kBlockWaves - 1) / kBlockWaves, tu.qsgd_blocks_per_cu);
     if (tu.qsgd_nt && tu.qsgd_rcp)
@@ -882,20 +933,24 @@ void launch_fused(const gcq_tuning &tu, const float *g, uint32_t s, uint32_t k0,
     else
         qsgd_fused_kernel<CC, H, false, false, Max>
             <<<grid, kBlockThreads, 0, stream>>>(g, s, k0, k1, norms, nibbles, nb_done);
+    if (n > nb_done * D)   // a short last bucket
+        qsgd_tail_kernel<Max><<<1, kWave, 0, stream>>>(g, n, nb_done * D, nb_done, s, k0, k1, norms,
+                                                      nibbles);
 }
 
 // Buckets per wavefront: the knob (0: as many as make 4 float4 chunks per
 // lane, which measured fastest), limited to C H <= 4 chunks per lane
 // (register budget).
 template <bool Max>
-void launch_fused_c(uint32_t C, const gcq_tuning &tu, const float *g, uint32_t s, uint32_t k0,
-                    uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
+void launch_fused_c(uint32_t C, const gcq_tuning &tu, const float *g, uint64_t n, uint32_t s,
+                    uint32_t k0, uint32_t k1, float *norms, uint32_t *nibbles, uint64_t nb_done,
                     hipStream_t stream)
 {
     const uint32_t hmax = C <= 4 ? 4u / C : 1u;
     const uint32_t want = tu.qsgd_buckets_per_wave ? (uint32_t)tu.qsgd_buckets_per_wave : hmax;
     const uint32_t H = want < hmax ? want : hmax;
-#define GCQ_F(CC, HH) launch_fused<CC, HH, Max>(tu, g, s, k0, k1, norms, nibbles, nb_done, stream)
+#define GCQ_F(CC, HH) \
+    launch_fused<CC, HH, Max>(tu, g, n, s, k0, k1, norms, nibbles, nb_done, stream)
     switch (C) {
     case 1:
         if (H >= 4)
@@ -930,17 +985,16 @@ hipError_t launch_qsgd_quantize(const float *g, uint64_t n, uint32_t d, uint32_t
     const uint64_t nwords = (n + 7) >> 3;
     uint64_t nb_done = 0;  // buckets (and their words) finished by the fused kernel
     const uint32_t C = d % 256u == 0 ? d / 256u : 0u;
-    if (C == 1 || C == 2 || C == 4 || C == 8) {
-        nb_done = n / d;
-        if (nb_done) {
-            if (maxnorm)
-                launch_fused_c<true>(C, tu, g, s, k0, k1, norms, nibbles, nb_done, stream);
-            else
-                launch_fused_c<false>(C, tu, g, s, k0, k1, norms, nibbles, nb_done, stream);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess)
-                return e;
-        }
+    if ((C == 1 || C == 2 || C == 4 || C == 8) && n >= d) {
+        // the full buckets, then a short last one in a one-wavefront launch
+        if (maxnorm)
+            launch_fused_c<true>(C, tu, g, n, s, k0, k1, norms, nibbles, n / d, stream);
+        else
+            launch_fused_c<false>(C, tu, g, n, s, k0, k1, norms, nibbles, n / d, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        nb_done = nb;
     }
     if (nb_done < nb) {
         const uint64_t left = nb - nb_done;
