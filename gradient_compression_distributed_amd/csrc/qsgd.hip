@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kWave) void qsgd_tail_kernel(const float *__restric
 // A NaN does not enter that scale, so a bucket holding one takes the exact
 // level path (the division-free shortcut assumes finite inputs).
 template <int C, int H, bool NT, bool Rcp, bool Max>
-__global__ __launch_bounds__(kBlockThreads, 7) void qsgd_fused_kernel(
+__global__ __launch_bounds__(kBlockThreads, C * H > 4 ? 4 : 7) void qsgd_fused_kernel(
     const float *__restrict__ g, uint32_t s, uint32_t k0, uint32_t k1, float *__restrict__ norms,
     uint32_t *__restrict__ nib, uint64_t nb_full)
 {
