@@ -110,25 +110,24 @@ __device__ __forceinline__ uint32_t coord_mask8(uint32_t w)
 }
 
 // Code bits of a nibble word's coordinates except the omega code of its
-// first coordinate's distance (which depends on earlier words):
+// first coordinate's distance (which depends on earlier words), from
+// nz = nonzero_nibbles(w) (bit 4k set: nibble k, coordinate 7 - k, coded):
 //   sign + omega(level): 1 + L(level) = 2, 4 or 7 bits for levels 1, 2-3,
 //   4-7, counted with popcounts of the level bits;
 //   omega(gap) for each later coordinate of the word, gap <= 7: L = 1, 3 or
 //   6, i.e. 1 + 2 [gap >= 2] + 3 [gap >= 4], where gap >= 2 means the
-//   coordinate just before is not coded, gap >= 4 the three before.
-__device__ __forceinline__ uint32_t word_code_bits(uint32_t w, uint32_t m8)
+//   coordinate just before (one nibble higher) is not coded, gap >= 4 the
+//   three before.
+__device__ __forceinline__ uint32_t word_code_bits(uint32_t w, uint32_t nz)
 {
-    const uint32_t nz = nonzero_nibbles(w);
     const uint32_t ge2 = ((w >> 1) | (w >> 2)) & 0x11111111u;
     const uint32_t ge4 = (w >> 2) & 0x11111111u;
-    uint32_t bits = 2u * (uint32_t)__builtin_popcount(nz) + 2u * (uint32_t)__builtin_popcount(ge2) +
-                    3u * (uint32_t)__builtin_popcount(ge4);
-    const uint32_t rest = m8 ? m8 & ~(0x80000000u >> (uint32_t)__builtin_clz(m8)) : 0u;
-    const uint32_t gap2 = rest & ~(m8 >> 1);
-    const uint32_t gap4 = gap2 & ~(m8 >> 2) & ~(m8 >> 3);
-    bits += (uint32_t)__builtin_popcount(rest) + 2u * (uint32_t)__builtin_popcount(gap2) +
-            3u * (uint32_t)__builtin_popcount(gap4);
-    return bits;
+    const uint32_t rest = nz ? nz & ~(0x80000000u >> (uint32_t)__builtin_clz(nz)) : 0u;
+    const uint32_t gap2 = rest & ~(nz >> 4);
+    const uint32_t gap4 = gap2 & ~(nz >> 8) & ~(nz >> 12);
+    return 2u * (uint32_t)__builtin_popcount(nz) + 2u * (uint32_t)__builtin_popcount(ge2) +
+           3u * (uint32_t)__builtin_popcount(ge4) + (uint32_t)__builtin_popcount(rest) +
+           2u * (uint32_t)__builtin_popcount(gap2) + 3u * (uint32_t)__builtin_popcount(gap4);
 }
 
 // Encode: one lane per bucket, a wavefront per 64 consecutive buckets (the
@@ -202,12 +201,14 @@ __global__ __launch_bounds__(kBlockThreads) void elias_length_kernel(
             for (uint32_t q = 0; q < 4; ++q) {
                 const uint32_t j = 4u * (k0 + t) + q;
                 const uint32_t w = clip_word(word_of(blk[t], q), j, blen);
-                const uint32_t m8 = coord_mask8(w);
-                const int32_t first = (int32_t)(8u * j + (uint32_t)__builtin_clz(m8 | 1u) - 24u);
-                const int32_t gap = first - prev > 1 ? first - prev : 1;   // >= 1 when m8 != 0
-                const uint32_t add = word_code_bits(w, m8) + omega_len_fast((uint32_t)gap);
-                bits += m8 ? add : 0u;
-                prev = m8 ? (int32_t)(8u * j + 7u - (uint32_t)__builtin_ctz(m8)) : prev;
+                const uint32_t nz = nonzero_nibbles(w);
+                // the word's first and last coded coordinates: its highest and
+                // lowest set bits (bit 4k is coordinate 7 - k)
+                const int32_t first = (int32_t)(8u * j + ((uint32_t)__builtin_clz(nz | 1u) >> 2));
+                const int32_t gap = first - prev > 1 ? first - prev : 1;   // >= 1 when nz != 0
+                const uint32_t add = word_code_bits(w, nz) + omega_len_fast((uint32_t)gap);
+                bits += nz ? add : 0u;
+                prev = nz ? (int32_t)(8u * j + 7u - ((uint32_t)__builtin_ctz(nz) >> 2)) : prev;
             }
         }
     }
